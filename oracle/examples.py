@@ -1,0 +1,77 @@
+"""The pages' worked examples, computed with the oracle (test infrastructure only).
+
+* ``two_tiles`` - "Fine-Grained Quantization in DeepSeek", worked example:
+  one 128-value tile centred near 0.1 and one containing a 20.0 outlier;
+  reconstruction error under one global scale versus one scale per tile, and
+  scale bytes per activation value.
+* ``per_tensor_vs_fine`` - "FP8 Mixed Precision: DeepSeek-V3 Training
+  Architecture", Step 2: 64 tokens x 512 channels of 0.4 * N(0, 1) with +35
+  added to channel 88, weights 1024 x 512 of 0.08 * N(0, 1) (legacy numpy
+  seed 42); relative Frobenius error of the GEMM with one scale per tensor
+  versus 1x128 / 128x128 scales.  Codes are on the E4M3 grid here (the page's
+  simulation rounds to integers instead).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import e4m3, quant
+
+
+def _groups_quant(x32: np.ndarray):
+    """Quantize float32 groups x32[..., n]; return float64 reconstruction and scales."""
+    q, s, _, _ = quant._quantize_groups(x32)
+    return e4m3.decode(q) * s.astype(np.float64)[..., None], s
+
+
+def two_tiles(seed: int = 0):
+    """Tile A ~ 0.1 + 0.01 N(0,1); tile B the same with element 0 = 20.0 (BF16)."""
+    rng = np.random.default_rng(seed)
+    a = (0.1 + 0.01 * rng.standard_normal(128)).astype(np.float32)
+    b = (0.1 + 0.01 * rng.standard_normal(128)).astype(np.float32)
+    b[0] = 20.0
+    tiles = quant.bf16_to_f32(_f32_to_bf16(np.stack([a, b])))       # [2][128]
+    glob, s_glob = _groups_quant(tiles.reshape(1, 256))
+    loc, s_loc = _groups_quant(tiles)
+    x = tiles.astype(np.float64)
+    glob = glob.reshape(2, 128)
+
+    def rms_rel(rec, ref):
+        return float(np.sqrt(np.mean(((rec - ref) / ref) ** 2)))
+
+    return dict(
+        tiles=tiles, s_global=s_glob[0], s_local=s_loc,
+        q_global=e4m3.encode((tiles / s_glob[0]).astype(np.float32)),
+        q_local=e4m3.encode((tiles / s_loc[:, None]).astype(np.float32)),
+        err_global=[rms_rel(glob[i], x[i]) for i in range(2)],
+        err_local=[rms_rel(loc[i], x[i]) for i in range(2)],
+        abs_err_global=np.abs(glob - x), abs_err_local=np.abs(loc - x),
+        scale_bytes_per_value_global=4 / 256,
+        scale_bytes_per_value_local=4 / 128,
+    )
+
+
+def per_tensor_vs_fine():
+    """Relative GEMM error, per-tensor vs fine-grained scales, on the E4M3 grid."""
+    rs = np.random.RandomState(42)
+    X = rs.randn(64, 512) * 0.4
+    X[:, 88] += 35.0
+    W = rs.randn(1024, 512) * 0.08
+    Y_ref = X @ W.T
+    X32, W32 = X.astype(np.float32), W.astype(np.float32)
+    Xt, _ = _groups_quant(X32.reshape(1, -1))
+    Wt, _ = _groups_quant(W32.reshape(1, -1))
+    Y_t = Xt.reshape(X.shape) @ Wt.reshape(W.shape).T
+    Xf, _ = _groups_quant(X32.reshape(64, 4, 128))
+    Wb = W32.reshape(8, 128, 4, 128).transpose(0, 2, 1, 3).reshape(8, 4, 128 * 128)
+    Wf, _ = _groups_quant(Wb)
+    Wf = Wf.reshape(8, 4, 128, 128).transpose(0, 2, 1, 3).reshape(1024, 512)
+    Y_f = Xf.reshape(X.shape) @ Wf.T
+    err_t = np.linalg.norm(Y_t - Y_ref) / np.linalg.norm(Y_ref)
+    err_f = np.linalg.norm(Y_f - Y_ref) / np.linalg.norm(Y_ref)
+    return dict(err_per_tensor=float(err_t), err_fine=float(err_f))
+
+
+def _f32_to_bf16(x):
+    b = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)

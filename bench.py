@@ -1,0 +1,315 @@
+"""Throughput of the fine-grained FP8 hot path on one MI355X.
+
+One step runs every row of the path once, back to back on one stream, on
+seeded synthetic inputs already resident in HBM:
+
+  quantizer  1x128 online quantization of X 8192x7168 (outliers in 16 channels)
+  fprop      1x128 quantization of X 4096x7168 + block-scaled GEMM
+             Y = X W^T 4096x18432x7168 (W pre-quantized 128x128), BF16 out
+  backward   dY 4096x18432: 1x128 quantization + Dgrad dX = dY W (W read
+             transposed); 128x1 quantization of dY and X + Wgrad dW = dY^T X
+             (FP32 out)
+  grouped    1x128 quantization of X 16384x7168 + one grouped launch over 8
+             experts (multinomial token counts), W_e 2048x7168
+  weights    128x128 quantization of W 18432x7168
+  policy     one caller-scale (history policy) quantization of a 128x7168 tile
+             with amax and saturation count, plus the history update
+
+`value` is the metric's headline: TFLOP/s of the fprop row including its
+quantization (2*M*N*K / (t_quant + t_gemm)), from HIP events on the launch
+stream averaged over the timed steps.  Other rows are reported under "rows".
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOP/s incl. fused 1x128 quant; quantizer GB/s"
+PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 MFMA
+PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=2048)
+    ap.add_argument("--only", default="", help="comma list of rows to run (default all)")
+    return ap.parse_args()
+
+
+def to_dev(a, torch):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if t.dtype == torch.uint16:
+        t = t.view(torch.int16)
+    return t.cuda()
+
+
+class Timer:
+    """HIP events on the current stream around named regions of each step."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+        self.acc = {}
+        self.count = {}
+
+    def region(self, name, fn):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        out = fn()
+        ev1.record()
+        self.pending.append((name, ev0, ev1))
+        return out
+
+    def collect(self):
+        self.torch.cuda.synchronize()
+        for name, a, b in self.pending:
+            self.acc[name] = self.acc.get(name, 0.0) + a.elapsed_time(b)
+            self.count[name] = self.count.get(name, 0) + 1
+        self.pending.clear()
+
+    def mean_ms(self, name):
+        return self.acc[name] / self.count[name]
+
+    def reset(self):
+        self.pending.clear()
+        self.acc.clear()
+        self.count.clear()
+
+
+def traffic_from_profiles(kernel_src):
+    """HBM bytes per launch from the committed PMC summary, if the kernel
+    source it was taken from is unchanged; else None."""
+    path = os.path.join(ROOT, "profiles", "fprop_gemm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != digest:
+            return None
+        return rec.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(x_bits, w_bits, sample_rows):
+    """Oracle (numpy, float64) on a bounded sample of the fprop workload:
+    1x128 quantization of the first `sample_rows` rows of X and their block
+    GEMM against the first 4096 rows of W (pre-quantized by the oracle,
+    untimed)."""
+    from oracle import gemm as og
+    from oracle import quant
+    K, Ns = 7168, 4096
+    xb = x_bits[:sample_rows]
+    Wq, sW = quant.quant_weight(w_bits[:Ns])
+    t0 = time.perf_counter()
+    Xq, sX = quant.quant_rows(xb)
+    og.fprop(Xq, sX, Wq, sW)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * sample_rows * Ns * K
+    cores = len(os.sched_getaffinity(0))
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"1x128 quant of {sample_rows}x{K} X rows + float64 block GEMM against "
+                      f"{Ns}x{K} pre-quantized W ({flop:.3e} FLOP, {dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fine_grained_fp8_amd as fp8
+    import synthetic as syn
+
+    fp8.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    only = set(s for s in args.only.split(",") if s)
+    want = (lambda r: not only or r in only)
+
+    # ---------------- inputs (seeded, synthetic, resident in HBM) ----------------
+    t0 = time.time()
+    d = {}
+    if want("quantizer"):
+        d["x2"] = to_dev(syn.activation_with_outliers(8192, 7168, seed=0), torch)
+    host = {}
+    if want("fprop") or want("backward") or want("weights"):
+        host["w3"] = syn.gaussian((18432, 7168), seed=1, std=0.02)
+        d["w3"] = to_dev(host["w3"], torch)
+    if want("fprop") or want("backward"):
+        host["x3"] = syn.activation_with_outliers(4096, 7168, seed=0)
+        d["x3"] = to_dev(host["x3"], torch)
+        d["wq3"], d["ws3"], _ = fp8.quant_weight_128x128(d["w3"])         # pre-quantized, untimed
+    if want("backward"):
+        d["dy4"] = to_dev(syn.gaussian((4096, 18432), seed=4, std=1e-3), torch)
+    if want("grouped"):
+        counts = syn.expert_counts(16384, 8, seed=0)
+        d["off5"] = to_dev(syn.expert_offsets(counts).astype(np.int32), torch)
+        d["x5"] = to_dev(syn.activation_with_outliers(16384, 7168, seed=0), torch)
+        wq5, ws5 = [], []
+        for e in range(8):
+            q, s, _ = fp8.quant_weight_128x128(to_dev(syn.gaussian((2048, 7168), seed=100 + e, std=0.02), torch))
+            wq5.append(q); ws5.append(s)
+        d["wq5"] = torch.stack(wq5).contiguous()
+        d["ws5"] = torch.stack(ws5).contiguous()
+        d["counts5"] = counts
+    if want("policy"):
+        steps = list(syn.drift_sequence(steps=2, M=128, K=7168, seed=0, spike_step=1))
+        d["xp"] = to_dev(steps[1][2], torch)
+        d["hist"] = torch.ones((56, 128), dtype=torch.float32, device="cuda")
+        d["sp"] = torch.ones((56, 128), dtype=torch.float32, device="cuda")
+        d["sat"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    tm = Timer(torch)
+
+    def step():
+        if want("quantizer"):
+            tm.region("quantizer", lambda: fp8.quant_act_1x128(d["x2"], "row"))
+        if want("fprop"):
+            ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
+            q, s, _ = tm.region("fprop.quant", lambda: fp8.quant_act_1x128(d["x3"], "row"))
+            tm.region("fprop.gemm", lambda: fp8.block_gemm("fprop", q, s, d["wq3"], d["ws3"]))
+            ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
+            tm.pending.append(("fprop", ev0, ev1))
+        if want("backward"):
+            ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
+            dq, ds, _ = tm.region("dgrad.quant", lambda: fp8.quant_act_1x128(d["dy4"], "row"))
+            tm.region("dgrad.gemm", lambda: fp8.block_gemm("dgrad", dq, ds, d["wq3"], d["ws3"]))
+            dqt, dst, _ = tm.region("wgrad.quant_dy", lambda: fp8.quant_act_1x128(d["dy4"], "col"))
+            xqt, xst, _ = tm.region("wgrad.quant_x", lambda: fp8.quant_act_1x128(d["x3"], "col"))
+            tm.region("wgrad.gemm", lambda: fp8.block_gemm("wgrad", dqt, dst, xqt, xst,
+                                                           out_dtype=torch.float32))
+            ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
+            tm.pending.append(("backward", ev0, ev1))
+        if want("grouped"):
+            ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
+            q, s, _ = tm.region("grouped.quant", lambda: fp8.quant_act_1x128(d["x5"], "row"))
+            tm.region("grouped.gemm", lambda: fp8.block_gemm_grouped(d["off5"], q, s, d["wq5"], d["ws5"]))
+            ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
+            tm.pending.append(("grouped", ev0, ev1))
+        if want("weights"):
+            tm.region("weights", lambda: fp8.quant_weight_128x128(d["w3"], transposed=False))
+        if want("policy"):
+            def pol():
+                fp8.quant_act_1x128(d["xp"], "row", scales_in=d["sp"], return_amax=True,
+                                    sat_count=d["sat"])
+            tm.region("policy", pol)
+
+    for _ in range(args.warmup):
+        step()
+        tm.collect()
+    tm.reset()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step()
+        if (i + 1) % 5 == 0:
+            tm.collect()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    tm.collect()
+    log(f"timed {args.steps} steps in {wall:.2f} s")
+
+    rows = {}
+    if want("quantizer"):
+        B = 8192 * 7168 * (2 + 1) + (7168 // 128) * 8192 * 4
+        t = tm.mean_ms("quantizer")
+        rows["quantizer"] = {"ms": t, "GB/s": B / t / 1e6, "bytes": B,
+                             "hbm_frac": B / t / 1e6 / PEAK_HBM_GBPS}
+    F3 = 2.0 * 4096 * 18432 * 7168
+    value = None
+    roofline = None
+    if want("fprop"):
+        tq, tg, tt = tm.mean_ms("fprop.quant"), tm.mean_ms("fprop.gemm"), tm.mean_ms("fprop")
+        value = F3 / (tq + tg) / 1e9
+        rows["fprop"] = {"ms_quant": tq, "ms_gemm": tg, "ms_region": tt,
+                         "TFLOP/s_incl_quant": value, "TFLOP/s_gemm": F3 / tg / 1e9,
+                         "quant_GB/s": 4096 * 7168 * (3 + 4 / 128) / tq / 1e6}
+        achieved = F3 / tg / 1e9
+        traffic = traffic_from_profiles(os.path.join(ROOT, "fine_grained_fp8_amd", "csrc", "gemm.hip"))
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / PEAK_FP8_TFLOPS, "traffic": traffic,
+                    "kernel": "block_gemm_kernel<FPROP,bf16> 4096x18432x7168",
+                    "algorithmic_flop_per_launch": F3}
+    if want("backward"):
+        tq1, tg1 = tm.mean_ms("dgrad.quant"), tm.mean_ms("dgrad.gemm")
+        tq2, tq3, tg2 = tm.mean_ms("wgrad.quant_dy"), tm.mean_ms("wgrad.quant_x"), tm.mean_ms("wgrad.gemm")
+        rows["dgrad"] = {"ms_quant": tq1, "ms_gemm": tg1, "TFLOP/s_incl_quant": F3 / (tq1 + tg1) / 1e9,
+                         "TFLOP/s_gemm": F3 / tg1 / 1e9}
+        rows["wgrad"] = {"ms_quant_dy_col": tq2, "ms_quant_x_col": tq3, "ms_gemm": tg2,
+                         "TFLOP/s_incl_quant": F3 / (tq2 + tq3 + tg2) / 1e9, "TFLOP/s_gemm": F3 / tg2 / 1e9,
+                         "col_quant_GB/s": (4096 * 18432 + 4096 * 7168) * (3 + 4 / 128) / (tq2 + tq3) / 1e6}
+    if want("grouped"):
+        F5 = 2.0 * 16384 * 2048 * 7168
+        tq, tg = tm.mean_ms("grouped.quant"), tm.mean_ms("grouped.gemm")
+        rows["grouped"] = {"ms_quant": tq, "ms_gemm": tg, "TFLOP/s_incl_quant": F5 / (tq + tg) / 1e9,
+                           "TFLOP/s_gemm": F5 / tg / 1e9, "tokens_per_expert": [int(c) for c in d["counts5"]]}
+    if want("weights"):
+        B = 18432 * 7168 * 3 + (18432 // 128) * (7168 // 128) * 4
+        t = tm.mean_ms("weights")
+        rows["weights"] = {"ms": t, "GB/s": B / t / 1e6}
+    if want("policy"):
+        rows["policy"] = {"ms": tm.mean_ms("policy")}
+
+    cpu = None
+    if not args.no_cpu_baseline and want("fprop"):
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(host["x3"], host["w3"], args.cpu_sample_rows)
+
+    if value is None and "quantizer" in rows:
+        value = rows["quantizer"]["GB/s"]
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s" if want("fprop") else "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "fprop: 1x128 quant of X 4096x7168 + block-scaled FP8 GEMM "
+                               "Y=X W^T 4096x18432x7168, BF16 out (W pre-quantized 128x128)",
+                   "M": 4096, "N": 18432, "K": 7168},
+        "roofline": roofline,
+        "roofline_quantizer": ({"bound": "hbm", "achieved": rows["quantizer"]["GB/s"], "peak": PEAK_HBM_GBPS,
+                                "unit": "GB/s", "frac": rows["quantizer"]["hbm_frac"], "traffic": None,
+                                "kernel": "quant_rows_kernel<online> 8192x7168"}
+                               if "quantizer" in rows else None),
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

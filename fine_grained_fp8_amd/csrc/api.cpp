@@ -1,0 +1,268 @@
+// C ABI of libfp8bs.so: host-side validation, device check, dispatch to the
+// kernel launchers.  Declarations and full contracts: include/fp8bs.h.
+#include "fp8bs.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "kernels.hpp"
+
+namespace {
+
+using fp8bs::GemmProblem;
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other
+std::atomic<int> g_device_kind[kMaxDevices];
+
+fp8_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return FP8_ERR_DEVICE;
+  }
+  if (dev >= kMaxDevices) return FP8_ERR_DEVICE;
+  int kind = g_device_kind[dev].load(std::memory_order_relaxed);
+  if (kind == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return FP8_ERR_DEVICE;
+    }
+    kind = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_kind[dev].store(kind, std::memory_order_relaxed);
+  }
+  return kind == 1 ? FP8_OK : FP8_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// [lo, hi) byte range of a row-major matrix with `rows` rows of `row_bytes`
+// at stride `ld_bytes`.
+struct Range {
+  uintptr_t lo, hi;
+};
+Range span(const void* p, int64_t rows, int64_t row_bytes, int64_t ld_bytes) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  if (rows <= 0 || row_bytes <= 0) return {b, b};
+  return {b, b + static_cast<uintptr_t>((rows - 1) * ld_bytes + row_bytes)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+fp8_status launched(hipError_t e) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return FP8_ERR_LAUNCH;
+  }
+  return FP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_abi_version(void) { return FP8BS_ABI_VERSION; }
+
+const char* fp8_status_string(fp8_status s) {
+  switch (s) {
+    case FP8_OK: return "ok";
+    case FP8_ERR_NULL: return "a required pointer is NULL";
+    case FP8_ERR_SHAPE: return "invalid shape (negative size, or a dimension is not a multiple of 128 where required)";
+    case FP8_ERR_LD: return "leading dimension smaller than the row length";
+    case FP8_ERR_ALIGN: return "pointer or row stride not 16-byte aligned";
+    case FP8_ERR_UNSUPPORTED: return "unsupported enum value or argument combination";
+    case FP8_ERR_DEVICE: return "no current HIP device, or the device is not gfx950";
+    case FP8_ERR_LAUNCH: return "kernel launch failed";
+    case FP8_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+  }
+  return "unknown status";
+}
+
+fp8_status fp8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                               fp8_tile_dir dir, uint8_t* q, int64_t ldq,
+                               float* scales, int64_t ld_s, const float* scales_in,
+                               float* amax_out, uint32_t* sat_count, void* stream) {
+  if (dir != FP8_TILE_ROW && dir != FP8_TILE_COL) return FP8_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
+  if (dir == FP8_TILE_ROW && cols % 128 != 0) return FP8_ERR_SHAPE;
+  if (dir == FP8_TILE_COL && rows % 128 != 0) return FP8_ERR_SHAPE;
+  if (dir == FP8_TILE_COL && (scales_in || sat_count)) return FP8_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return FP8_OK;
+  if (!x || !q) return FP8_ERR_NULL;
+  if (!scales_in && !scales) return FP8_ERR_NULL;
+  const int64_t out_rows = dir == FP8_TILE_ROW ? rows : cols;
+  const int64_t out_cols = dir == FP8_TILE_ROW ? cols : rows;
+  const int64_t s_rows = dir == FP8_TILE_ROW ? cols / 128 : rows / 128;
+  const int64_t s_cols = dir == FP8_TILE_ROW ? rows : cols;
+  if (ldx < cols || ldq < out_cols || ld_s < s_cols) return FP8_ERR_LD;
+  if (!aligned16(x) || !aligned16(q) || (ldx * 2) % 16 != 0 || ldq % 16 != 0) return FP8_ERR_ALIGN;
+  if ((scales && !aligned4(scales)) || (scales_in && !aligned4(scales_in)) ||
+      (amax_out && !aligned4(amax_out)) || (sat_count && !aligned4(sat_count)))
+    return FP8_ERR_ALIGN;
+  const Range rx = span(x, rows, cols * 2, ldx * 2);
+  const Range rq = span(q, out_rows, out_cols, ldq);
+  const Range rs = span(scales ? (const void*)scales : (const void*)scales_in, s_rows, s_cols * 4, ld_s * 4);
+  if (overlap(rq, rx)) return FP8_ERR_ALIAS;
+  if (scales && (overlap(rs, rx) || overlap(rs, rq))) return FP8_ERR_ALIAS;
+  if (amax_out) {
+    const Range ra = span(amax_out, s_rows, s_cols * 4, ld_s * 4);
+    if (overlap(ra, rx) || overlap(ra, rq) || (scales && overlap(ra, rs))) return FP8_ERR_ALIAS;
+    if (scales_in && overlap(ra, span(scales_in, s_rows, s_cols * 4, ld_s * 4))) return FP8_ERR_ALIAS;
+  }
+  if (scales_in && overlap(rq, span(scales_in, s_rows, s_cols * 4, ld_s * 4))) return FP8_ERR_ALIAS;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (dir == FP8_TILE_ROW)
+    return launched(fp8bs::launch_quant_rows(xb, rows, cols, ldx, q, ldq, scales_in ? nullptr : scales,
+                                             ld_s, scales_in, amax_out, sat_count, st));
+  return launched(fp8bs::launch_quant_cols(xb, rows, cols, ldx, q, ldq, scales, ld_s, amax_out, st));
+}
+
+fp8_status fp8_quant_weight_128x128(const void* w, int64_t rows, int64_t cols, int64_t ldw,
+                                    uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
+                                    float* scales, int64_t ld_s, void* stream) {
+  if (rows < 0 || cols < 0 || rows % 128 != 0 || cols % 128 != 0) return FP8_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8_OK;
+  if (!w || !q || !scales) return FP8_ERR_NULL;
+  if (ldw < cols || ldq < cols || ld_s < cols / 128 || (q_t && ldq_t < rows)) return FP8_ERR_LD;
+  if (!aligned16(w) || !aligned16(q) || (ldw * 2) % 16 != 0 || ldq % 16 != 0 || !aligned4(scales))
+    return FP8_ERR_ALIGN;
+  if (q_t && (!aligned16(q_t) || ldq_t % 16 != 0)) return FP8_ERR_ALIGN;
+  const Range rw = span(w, rows, cols * 2, ldw * 2);
+  const Range rq = span(q, rows, cols, ldq);
+  const Range rs = span(scales, rows / 128, (cols / 128) * 4, ld_s * 4);
+  if (overlap(rq, rw) || overlap(rs, rw) || overlap(rs, rq)) return FP8_ERR_ALIAS;
+  if (q_t) {
+    const Range rt = span(q_t, cols, rows, ldq_t);
+    if (overlap(rt, rw) || overlap(rt, rq) || overlap(rt, rs)) return FP8_ERR_ALIAS;
+  }
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  return launched(fp8bs::launch_quant_weight(static_cast<const uint16_t*>(w), rows, cols, ldw, q, ldq,
+                                             q_t, ldq_t, scales, ld_s,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+static fp8_status validate_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                                       int64_t lda, const float* sA, int64_t ld_sa,
+                                       const uint8_t* B, const float* sB, void* C,
+                                       fp8_out_dtype c_dtype, int64_t ldc) {
+  if (c_dtype != FP8_OUT_BF16 && c_dtype != FP8_OUT_FP32) return FP8_ERR_UNSUPPORTED;
+  if (M < 0 || N <= 0 || K <= 0 || K % 128 != 0) return FP8_ERR_SHAPE;
+  if (M == 0) return FP8_OK;
+  if (!A || !sA || !B || !sB || !C) return FP8_ERR_NULL;
+  if (lda < K || ld_sa < M || ldc < N) return FP8_ERR_LD;
+  // the kernels address one 256-row tile with 32-bit byte offsets
+  if (lda > (int64_t{1} << 23)) return FP8_ERR_UNSUPPORTED;
+  const int64_t esz = c_dtype == FP8_OUT_FP32 ? 4 : 2;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C) || lda % 16 != 0 || (ldc * esz) % 16 != 0 ||
+      !aligned4(sA) || !aligned4(sB))
+    return FP8_ERR_ALIGN;
+  return FP8_OK;
+}
+
+fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t K,
+                          const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
+                          const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
+                          void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream) {
+  if (layout != FP8_LAYOUT_FPROP && layout != FP8_LAYOUT_DGRAD && layout != FP8_LAYOUT_WGRAD)
+    return FP8_ERR_UNSUPPORTED;
+  fp8_status st = validate_gemm_common(M, N, K, A, lda, sA, ld_sa, B, sB, C, c_dtype, ldc);
+  if (st != FP8_OK || M == 0) return st;
+  if (layout != FP8_LAYOUT_WGRAD && N % 128 != 0) return FP8_ERR_SHAPE;
+  int64_t b_rows, b_cols, sb_rows, sb_cols;
+  switch (layout) {
+    case FP8_LAYOUT_FPROP: b_rows = N; b_cols = K; sb_rows = N / 128; sb_cols = K / 128; break;
+    case FP8_LAYOUT_DGRAD: b_rows = K; b_cols = N; sb_rows = K / 128; sb_cols = N / 128; break;
+    default: b_rows = N; b_cols = K; sb_rows = K / 128; sb_cols = N; break;
+  }
+  if (ldb < b_cols || ld_sb < sb_cols) return FP8_ERR_LD;
+  if (ldb % 16 != 0) return FP8_ERR_ALIGN;
+  if (ldb > (int64_t{1} << 23)) return FP8_ERR_UNSUPPORTED;
+  if (layout == FP8_LAYOUT_DGRAD && K * ldb >= (int64_t{1} << 31)) return FP8_ERR_UNSUPPORTED;
+  const int64_t esz = c_dtype == FP8_OUT_FP32 ? 4 : 2;
+  const Range rc = span(C, M, N * esz, ldc * esz);
+  if (overlap(rc, span(A, M, K, lda)) || overlap(rc, span(B, b_rows, b_cols, ldb)) ||
+      overlap(rc, span(sA, K / 128, M * 4, ld_sa * 4)) ||
+      overlap(rc, span(sB, sb_rows, sb_cols * 4, ld_sb * 4)))
+    return FP8_ERR_ALIAS;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  GemmProblem p{};
+  p.layout = static_cast<int>(layout);
+  p.M = M; p.N = N; p.K = K;
+  p.A = A; p.lda = lda; p.sA = sA; p.ld_sa = ld_sa;
+  p.B = B; p.ldb = ldb; p.sB = sB; p.ld_sb = ld_sb;
+  p.C = C; p.ldc = ldc; p.out_fp32 = c_dtype == FP8_OUT_FP32;
+  p.groups = 0; p.offsets = nullptr;
+  return launched(fp8bs::launch_gemm(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+fp8_status fp8_block_gemm_grouped(int32_t groups, const int32_t* offsets_dev, int64_t total_M,
+                                  int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                  const float* sA, int64_t ld_sa, const uint8_t* B, int64_t ldb,
+                                  const float* sB, void* C, fp8_out_dtype c_dtype, int64_t ldc,
+                                  void* stream) {
+  if (groups <= 0) return FP8_ERR_SHAPE;
+  fp8_status st = validate_gemm_common(total_M, N, K, A, lda, sA, ld_sa, B, sB, C, c_dtype, ldc);
+  if (st != FP8_OK || total_M == 0) return st;
+  if (!offsets_dev) return FP8_ERR_NULL;
+  if (!aligned4(offsets_dev)) return FP8_ERR_ALIGN;
+  if (N % 128 != 0) return FP8_ERR_SHAPE;
+  if (ldb < K) return FP8_ERR_LD;
+  if (ldb % 16 != 0) return FP8_ERR_ALIGN;
+  if (ldb > (int64_t{1} << 23)) return FP8_ERR_UNSUPPORTED;
+  const int64_t esz = c_dtype == FP8_OUT_FP32 ? 4 : 2;
+  const Range rc = span(C, total_M, N * esz, ldc * esz);
+  if (overlap(rc, span(A, total_M, K, lda)) ||
+      overlap(rc, span(B, static_cast<int64_t>(groups) * N, K, ldb)) ||
+      overlap(rc, span(sA, K / 128, total_M * 4, ld_sa * 4)) ||
+      overlap(rc, span(sB, 1, static_cast<int64_t>(groups) * (N / 128) * (K / 128) * 4, 0)) ||
+      overlap(rc, span(offsets_dev, 1, (static_cast<int64_t>(groups) + 1) * 4, 0)))
+    return FP8_ERR_ALIAS;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  GemmProblem p{};
+  p.layout = FP8_LAYOUT_FPROP;
+  p.M = total_M; p.N = N; p.K = K;
+  p.A = A; p.lda = lda; p.sA = sA; p.ld_sa = ld_sa;
+  p.B = B; p.ldb = ldb; p.sB = sB; p.ld_sb = K / 128;
+  p.C = C; p.ldc = ldc; p.out_fp32 = c_dtype == FP8_OUT_FP32;
+  p.groups = groups; p.offsets = offsets_dev;
+  return launched(fp8bs::launch_gemm(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+fp8_status fp8_amax_history_update(float* hist, const float* amax, int64_t n, float decay,
+                                   int init, float* scales_out, void* stream) {
+  if (n < 0) return FP8_ERR_SHAPE;
+  if (n == 0) return FP8_OK;
+  if (!hist || !amax) return FP8_ERR_NULL;
+  if (!aligned4(hist) || !aligned4(amax) || (scales_out && !aligned4(scales_out))) return FP8_ERR_ALIGN;
+  const Range rh = span(hist, 1, n * 4, 0);
+  if (overlap(rh, span(amax, 1, n * 4, 0))) return FP8_ERR_ALIAS;
+  if (scales_out && (overlap(span(scales_out, 1, n * 4, 0), rh) ||
+                     overlap(span(scales_out, 1, n * 4, 0), span(amax, 1, n * 4, 0))))
+    return FP8_ERR_ALIAS;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  return launched(fp8bs::launch_history_update(hist, amax, n, decay, init, scales_out,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+fp8_status fp8_cast_e4m3(const float* x, int64_t n, uint8_t* q, void* stream) {
+  if (n < 0) return FP8_ERR_SHAPE;
+  if (n == 0) return FP8_OK;
+  if (!x || !q) return FP8_ERR_NULL;
+  if (!aligned4(x)) return FP8_ERR_ALIGN;
+  if (overlap(span(x, 1, n * 4, 0), span(q, 1, n, 0))) return FP8_ERR_ALIAS;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  return launched(fp8bs::launch_cast_e4m3(x, n, q, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

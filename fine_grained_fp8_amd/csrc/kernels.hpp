@@ -1,0 +1,52 @@
+// Host-side launchers of the HIP kernels (internal to libfp8bs.so).
+// Arguments are already validated by api.cpp; each launcher only sizes the
+// grid and enqueues on `stream`, returning the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bs {
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                             const float* scales_in, float* amax_out, uint32_t* sat_count,
+                             hipStream_t stream);
+
+hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                             float* amax_out, hipStream_t stream);
+
+hipError_t launch_quant_weight(const uint16_t* w, int64_t rows, int64_t cols, int64_t ldw,
+                               uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
+                               float* scales, int64_t ld_s, hipStream_t stream);
+
+hipError_t launch_history_update(float* hist, const float* amax, int64_t n, float decay, int init,
+                                 float* scales_out, hipStream_t stream);
+
+hipError_t launch_cast_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream);
+
+enum GemmLayout { kFprop = 0, kDgrad = 1, kWgrad = 2 };
+
+struct GemmProblem {
+  int layout;            // GemmLayout
+  int64_t M, N, K;
+  const uint8_t* A;      // token side (rows m), K-contiguous
+  int64_t lda;
+  const float* sA;       // [K/128][ld_sa]
+  int64_t ld_sa;
+  const uint8_t* B;      // weight side: [N][K] (FPROP, WGRAD) or [K][N] (DGRAD)
+  int64_t ldb;
+  const float* sB;
+  int64_t ld_sb;
+  void* C;
+  int64_t ldc;
+  int out_fp32;
+  // grouped FPROP: groups > 0
+  int groups;
+  const int32_t* offsets;
+};
+
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+
+}  // namespace fp8bs

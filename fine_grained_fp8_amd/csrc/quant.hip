@@ -1,0 +1,342 @@
+// Fine-grained FP8 quantizers for gfx950: 1x128 row tiles (online or with
+// caller scales), 128x1 column tiles with transposed output, 128x128 weight
+// blocks (optionally also writing the transposed codes), the amax-history
+// update of the delayed-scaling policy, and the bare saturating E4M3 cast.
+//
+// Sources: "Fine-Grained Quantization in DeepSeek" sections 2-3 (1x128 tiles,
+// 128x128 blocks, scale metadata produced efficiently and laid out for the
+// GEMM); "FP8 Mixed Precision: DeepSeek-V3 Training Architecture" section 1
+// (scale = block max / 448, clip to +-448); "Online Quantization During
+// Training" sections 2 and 5 (max, scale and cast fused in one pass, right
+// before the matmul).
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace fp8bs {
+
+// ---------------------------------------------------------------------------
+// 1x128 row tiles.  One wave owns 64 rows x one 128-column K block: 16 loads
+// of 4 tiles each (a tile is one 16-lane DPP row holding 8 BF16 per lane), so
+// the 64 scales of the block are written as one contiguous 256-byte store
+// into the MN-major scale array [K/128][ld_s].  A workgroup's four waves take
+// four consecutive K blocks of the same 64 rows.
+// ---------------------------------------------------------------------------
+template <bool kExternal>
+__global__ __launch_bounds__(256) void quant_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t kblocks,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int64_t ld_s,
+    const float* __restrict__ scales_in, float* __restrict__ amax_out,
+    uint32_t* __restrict__ sat_count) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t nkbg = (kblocks + 3) >> 2;
+  const int64_t rb = blockIdx.x / nkbg;
+  const int64_t kb = (blockIdx.x % nkbg) * 4 + wave;
+  if (kb >= kblocks) return;                 // whole wave idle; no block barriers below
+  const int sub = lane >> 4;
+  const int l16 = lane & 15;
+  const int64_t r0 = rb * 64;
+  const uint16_t* xb = x + kb * 128 + l16 * 8;
+
+  uint4 v[16];
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    const int64_t row = r0 + 4 * g + sub;
+    v[g] = row < rows ? *reinterpret_cast<const uint4*>(xb + row * ldx) : make_uint4(0, 0, 0, 0);
+  }
+
+  float my_s = 0.0f, my_amax = 0.0f;
+  uint32_t sat = 0;
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    const int64_t row = r0 + 4 * g + sub;
+    const uint32_t t = row16_max_u32(absmax_bits8(v[g]));
+    float s;
+    if constexpr (kExternal) {
+      s = row < rows ? scales_in[kb * ld_s + row] : 1.0f;
+    } else {
+      s = tile_scale(t);
+    }
+    const uint4 d = v[g];
+    uint2 out;
+    if (!kExternal && t < kBf16InfAbs) {
+      const float r = 1.0f / s;              // correctly rounded reciprocal
+      out.x = pack4_sat(div_by_scale(bf16_lo(d.x), s, r), div_by_scale(bf16_hi(d.x), s, r),
+                        div_by_scale(bf16_lo(d.y), s, r), div_by_scale(bf16_hi(d.y), s, r));
+      out.y = pack4_sat(div_by_scale(bf16_lo(d.z), s, r), div_by_scale(bf16_hi(d.z), s, r),
+                        div_by_scale(bf16_lo(d.w), s, r), div_by_scale(bf16_hi(d.w), s, r));
+    } else {
+      // Inf/NaN tiles, or caller scales of any value: plain IEEE division.
+      const float y0 = bf16_lo(d.x) / s, y1 = bf16_hi(d.x) / s;
+      const float y2 = bf16_lo(d.y) / s, y3 = bf16_hi(d.y) / s;
+      const float y4 = bf16_lo(d.z) / s, y5 = bf16_hi(d.z) / s;
+      const float y6 = bf16_lo(d.w) / s, y7 = bf16_hi(d.w) / s;
+      out.x = pack4_sat_nan(y0, y1, y2, y3);
+      out.y = pack4_sat_nan(y4, y5, y6, y7);
+      if constexpr (kExternal) {
+        if (row < rows) {
+          sat += (fabsf(y0) > 464.0f) + (fabsf(y1) > 464.0f) + (fabsf(y2) > 464.0f) +
+                 (fabsf(y3) > 464.0f) + (fabsf(y4) > 464.0f) + (fabsf(y5) > 464.0f) +
+                 (fabsf(y6) > 464.0f) + (fabsf(y7) > 464.0f);
+        }
+      }
+    }
+    if (row < rows) *reinterpret_cast<uint2*>(q + row * ldq + kb * 128 + l16 * 8) = out;
+    // lane j collects the scale of row r0 + j, held by lane 16 * (j % 4) in group j / 4
+    const float sg = __shfl(s, (lane & 3) * 16);
+    const float ag = __shfl(amax_value(t), (lane & 3) * 16);
+    if ((lane >> 2) == g) { my_s = sg; my_amax = ag; }
+  }
+  const int64_t row = r0 + lane;
+  if (row < rows) {
+    if (!kExternal) scales[kb * ld_s + row] = my_s;
+    if (amax_out) amax_out[kb * ld_s + row] = my_amax;
+  }
+  if constexpr (kExternal) {
+    if (sat_count) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) sat += __shfl_xor(sat, off);
+      if (lane == 0 && sat) atomicAdd(sat_count, sat);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x1 column tiles, transposed output.  A workgroup stages a 128-row x
+// 64-column BF16 block in LDS (coalesced 16-byte row loads), each thread
+// takes two adjacent columns x 16 rows, the column max is combined across the
+// eight row segments through LDS, and every column's 128 codes are written as
+// contiguous 16-byte pieces of the transposed output row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_cols_kernel(
+    const uint16_t* __restrict__ x, int64_t cols, int64_t ldx, int64_t ncb,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int64_t ld_s,
+    float* __restrict__ amax_out) {
+  __shared__ uint32_t tile[128][32];
+  __shared__ uint32_t red[8][32];
+  const int t = threadIdx.x;
+  const int64_t rb = blockIdx.x / ncb;
+  const int64_t c0 = (blockIdx.x % ncb) * 64;
+  const int64_t r0 = rb * 128;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = t + 256 * i;
+    const int row = ci >> 3, cc = ci & 7;
+    const int64_t col = c0 + cc * 8;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    const uint16_t* src = x + (r0 + row) * ldx + col;
+    if (col + 8 <= cols) {
+      val = *reinterpret_cast<const uint4*>(src);
+    } else if (col < cols) {                 // ragged last chunk: stay inside the row
+      uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int e = 0; e < 8 && col + e < cols; ++e) h[e] = src[e];
+      val = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    }
+    *reinterpret_cast<uint4*>(&tile[row][cc * 4]) = val;
+  }
+  __syncthreads();
+  const int p = t & 31, seg = t >> 5;
+  uint32_t d[16];
+  us2 m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    d[i] = tile[seg * 16 + i][p];
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[i] & 0x7FFF7FFFu));
+  }
+  red[seg][p] = __builtin_bit_cast(uint32_t, m);
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 8; ++s) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, red[s][p]));
+  const uint32_t ta = m.x, tb = m.y;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t tt = h ? tb : ta;
+    const float s = tile_scale(tt);
+    float y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = h ? bf16_hi(d[i]) : bf16_lo(d[i]);
+    uint4 out;
+    if (tt < kBf16InfAbs) {
+      const float r = 1.0f / s;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = div_by_scale(y[i], s, r);
+      out.x = pack4_sat(y[0], y[1], y[2], y[3]);
+      out.y = pack4_sat(y[4], y[5], y[6], y[7]);
+      out.z = pack4_sat(y[8], y[9], y[10], y[11]);
+      out.w = pack4_sat(y[12], y[13], y[14], y[15]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = y[i] / s;
+      out.x = pack4_sat_nan(y[0], y[1], y[2], y[3]);
+      out.y = pack4_sat_nan(y[4], y[5], y[6], y[7]);
+      out.z = pack4_sat_nan(y[8], y[9], y[10], y[11]);
+      out.w = pack4_sat_nan(y[12], y[13], y[14], y[15]);
+    }
+    const int64_t col = c0 + 2 * p + h;
+    if (col < cols) {
+      *reinterpret_cast<uint4*>(q + col * ldq + r0 + seg * 16) = out;
+      if (seg == 0) {
+        scales[rb * ld_s + col] = s;
+        if (amax_out) amax_out[rb * ld_s + col] = amax_value(tt);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight blocks: one workgroup per block, block max through DPP row
+// reduction, cross-row shuffles and LDS; optional transposed codes via an LDS
+// byte tile and 4x4 byte transposes (for the input-gradient GEMM).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_weight_kernel(
+    const uint16_t* __restrict__ w, int64_t ldw, int64_t nbk,
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ q_t, int64_t ldq_t,
+    float* __restrict__ scales, int64_t ld_s) {
+  __shared__ uint32_t wmax[4];
+  __shared__ uint32_t codes[128][32];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int64_t bi = blockIdx.x / nbk, bj = blockIdx.x % nbk;
+  const int64_t r0 = bi * 128, c0 = bj * 128;
+  uint4 v[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ci = t + 256 * i;
+    const int row = ci >> 4, cc = ci & 15;
+    v[i] = *reinterpret_cast<const uint4*>(w + (r0 + row) * ldw + c0 + cc * 8);
+    m = max(m, absmax_bits8(v[i]));
+  }
+  m = row16_max_u32(m);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+  if (lane == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float s = tile_scale(m);
+  if (t == 0) scales[bi * ld_s + bj] = s;
+  const bool fast = m < kBf16InfAbs;
+  const float r = fast ? 1.0f / s : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ci = t + 256 * i;
+    const int row = ci >> 4, cc = ci & 15;
+    const uint4 d = v[i];
+    uint2 out;
+    if (fast) {
+      out.x = pack4_sat(div_by_scale(bf16_lo(d.x), s, r), div_by_scale(bf16_hi(d.x), s, r),
+                        div_by_scale(bf16_lo(d.y), s, r), div_by_scale(bf16_hi(d.y), s, r));
+      out.y = pack4_sat(div_by_scale(bf16_lo(d.z), s, r), div_by_scale(bf16_hi(d.z), s, r),
+                        div_by_scale(bf16_lo(d.w), s, r), div_by_scale(bf16_hi(d.w), s, r));
+    } else {
+      out.x = pack4_sat_nan(bf16_lo(d.x) / s, bf16_hi(d.x) / s, bf16_lo(d.y) / s, bf16_hi(d.y) / s);
+      out.y = pack4_sat_nan(bf16_lo(d.z) / s, bf16_hi(d.z) / s, bf16_lo(d.w) / s, bf16_hi(d.w) / s);
+    }
+    *reinterpret_cast<uint2*>(q + (r0 + row) * ldq + c0 + cc * 8) = out;
+    if (q_t) {
+      codes[row][cc * 2] = out.x;
+      codes[row][cc * 2 + 1] = out.y;
+    }
+  }
+  if (!q_t) return;                          // uniform over the workgroup
+  __syncthreads();
+  const int cg = t & 31, rg = t >> 5;        // columns 4cg..4cg+3, rows 16rg..16rg+15
+  uint32_t o[4][4];
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) {
+    const int rr = rg * 16 + qd * 4;
+    transpose4x4_bytes(codes[rr][cg], codes[rr + 1][cg], codes[rr + 2][cg], codes[rr + 3][cg],
+                       o[qd][0], o[qd][1], o[qd][2], o[qd][3]);
+  }
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const uint4 val = make_uint4(o[0][jj], o[1][jj], o[2][jj], o[3][jj]);
+    *reinterpret_cast<uint4*>(q_t + (c0 + 4 * cg + jj) * ldq_t + r0 + 16 * rg) = val;
+  }
+}
+
+__global__ __launch_bounds__(256) void history_update_kernel(float* __restrict__ hist,
+                                                             const float* __restrict__ amax,
+                                                             int64_t n, float decay, int init,
+                                                             float* __restrict__ scales_out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float h;
+  if (init) {
+    h = amax[i];
+  } else {
+    const float one_minus = 1.0f - decay;
+    const float a = decay * hist[i];
+    const float b = one_minus * amax[i];
+    h = a + b;                                // separate roundings (no contraction)
+  }
+  hist[i] = h;
+  if (scales_out) {
+    float s = h / 448.0f;
+    s = __builtin_isnan(s) ? __uint_as_float(kCanonicalNaN) : fmaxf(s, scale_floor());
+    scales_out[i] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void cast_e4m3_kernel(const float* __restrict__ x, int64_t n,
+                                                        uint8_t* __restrict__ q) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    q[i] = (uint8_t)(pack4_sat_nan(x[i], 0.0f, 0.0f, 0.0f) & 0xFFu);
+  }
+}
+
+// ----------------------------- launchers -----------------------------------
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                             const float* scales_in, float* amax_out, uint32_t* sat_count,
+                             hipStream_t stream) {
+  const int64_t kblocks = cols / 128;
+  const int64_t nblocks = ((rows + 63) / 64) * ((kblocks + 3) / 4);
+  if (scales_in) {
+    hipLaunchKernelGGL(quant_rows_kernel<true>, dim3((unsigned)nblocks), dim3(256), 0, stream,
+                       x, rows, ldx, kblocks, q, ldq, scales, ld_s, scales_in, amax_out, sat_count);
+  } else {
+    hipLaunchKernelGGL(quant_rows_kernel<false>, dim3((unsigned)nblocks), dim3(256), 0, stream,
+                       x, rows, ldx, kblocks, q, ldq, scales, ld_s, scales_in, amax_out, sat_count);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                             float* amax_out, hipStream_t stream) {
+  const int64_t ncb = (cols + 63) / 64;
+  const int64_t nblocks = (rows / 128) * ncb;
+  hipLaunchKernelGGL(quant_cols_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream,
+                     x, cols, ldx, ncb, q, ldq, scales, ld_s, amax_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(const uint16_t* w, int64_t rows, int64_t cols, int64_t ldw,
+                               uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
+                               float* scales, int64_t ld_s, hipStream_t stream) {
+  const int64_t nbk = cols / 128;
+  const int64_t nblocks = (rows / 128) * nbk;
+  hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream,
+                     w, ldw, nbk, q, ldq, q_t, ldq_t, scales, ld_s);
+  return hipGetLastError();
+}
+
+hipError_t launch_history_update(float* hist, const float* amax, int64_t n, float decay, int init,
+                                 float* scales_out, hipStream_t stream) {
+  const int64_t nblocks = (n + 255) / 256;
+  hipLaunchKernelGGL(history_update_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream,
+                     hist, amax, n, decay, init, scales_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream) {
+  int64_t nblocks = (n + 255) / 256;
+  if (nblocks > 1048576) nblocks = 1048576;
+  hipLaunchKernelGGL(cast_e4m3_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, x, n, q);
+  return hipGetLastError();
+}
+
+}  // namespace fp8bs

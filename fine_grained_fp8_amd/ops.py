@@ -1,0 +1,183 @@
+"""Thin PyTorch-facing binding of libfp8bs.so (argument marshalling only).
+
+Tensors are used for device memory and the current HIP stream; every step of
+the computation runs in the library's kernels.  Names follow the C ABI in
+include/fp8bs.h.  Scale arrays are MN-major: [K/128][ld] with
+ld = round_up(rows, 4) for 1x128 row tiles.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+FP8_DTYPE = torch.uint8
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes_ptr(t)
+
+
+def ctypes_ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _check_2d(name, t, dtypes):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name}: expected a 2-D row-major tensor, got shape {tuple(t.shape)} "
+                         f"strides {t.stride()}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+
+
+def round_up(x: int, m: int) -> int:
+    return (x + m - 1) // m * m
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def quant_act_1x128(x: torch.Tensor, direction: str = "row", *, scales_in=None,
+                    return_amax: bool = False, sat_count=None, stream=None):
+    """Online FP8 quantization of activations.
+
+    direction "row": 1x128 tiles along each row; returns
+        q [rows][cols] uint8, scales [cols/128][round_up(rows, 4)] float32.
+    direction "col": 128x1 tiles along each column, transposed output; returns
+        q [cols][rows] uint8, scales [rows/128][round_up(cols, 4)] float32.
+    scales_in (row only): caller scales in the scale layout; then the returned
+    scales are None.  return_amax adds the per-tile max |x| (same layout).
+    sat_count: optional int32/uint32 device tensor of one element, incremented.
+    Returns (q, scales, amax_or_None).
+    """
+    lib = _lib.load_library()
+    _check_2d("x", x, _BF16)
+    rows, cols = x.shape
+    dev = x.device
+    if direction == "row":
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        s_shape = (cols // 128, round_up(rows, 4))
+        tile_dir = _lib.TILE_ROW
+    elif direction == "col":
+        q = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+        s_shape = (rows // 128, round_up(cols, 4))
+        tile_dir = _lib.TILE_COL
+    else:
+        raise ValueError(direction)
+    if scales_in is not None:
+        _check_2d("scales_in", scales_in, (torch.float32,))
+        scales = None
+        ld_s = scales_in.stride(0)
+    else:
+        scales = torch.empty(s_shape, dtype=torch.float32, device=dev)
+        ld_s = s_shape[1]
+    amax = torch.empty(s_shape if scales_in is None else tuple(scales_in.shape),
+                       dtype=torch.float32, device=dev) if return_amax else None
+    st = lib.fp8_quant_act_1x128(
+        _ptr(x), rows, cols, x.stride(0), tile_dir, _ptr(q), q.stride(0),
+        _ptr(scales), ld_s, _ptr(scales_in), _ptr(amax), _ptr(sat_count), _stream(stream))
+    _lib.check("fp8_quant_act_1x128", st)
+    return q, scales, amax
+
+
+def quant_weight_128x128(w: torch.Tensor, *, transposed: bool = False, stream=None):
+    """128x128 block quantization of weights [N][K].
+
+    Returns (q [N][K] uint8, scales [N/128][K/128] float32, q_t [K][N] or None).
+    """
+    lib = _lib.load_library()
+    _check_2d("w", w, _BF16)
+    rows, cols = w.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+    q_t = torch.empty((cols, rows), dtype=torch.uint8, device=w.device) if transposed else None
+    scales = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=w.device)
+    st = lib.fp8_quant_weight_128x128(
+        _ptr(w), rows, cols, w.stride(0), _ptr(q), q.stride(0), _ptr(q_t),
+        q_t.stride(0) if q_t is not None else 0, _ptr(scales), scales.stride(0), _stream(stream))
+    _lib.check("fp8_quant_weight_128x128", st)
+    return q, scales, q_t
+
+
+def block_gemm(layout: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor,
+               *, out_dtype=torch.bfloat16, out=None, stream=None):
+    """Block-scaled FP8 GEMM.
+
+    fprop: A [M][K], sA [K/128][>=M], B [N][K], sB [N/128][>=K/128]
+    dgrad: A [M][K], sA [K/128][>=M], B [K][N] (forward W_q), sB [K/128][>=N/128]
+    wgrad: A [M][K], sA [K/128][>=M], B [N][K], sB [K/128][>=N]
+    Returns C [M][N] in out_dtype (bfloat16 or float32).
+    """
+    lib = _lib.load_library()
+    for n, t in (("A", A), ("B", B)):
+        _check_2d(n, t, (torch.uint8, torch.float8_e4m3fn))
+    _check_2d("sA", sA, (torch.float32,))
+    _check_2d("sB", sB, (torch.float32,))
+    M, K = A.shape
+    N = B.shape[1] if layout == "dgrad" else B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    code = _lib.OUT_FP32 if out.dtype == torch.float32 else _lib.OUT_BF16
+    st = lib.fp8_block_gemm(
+        _lib.LAYOUT[layout], M, N, K, _ptr(A), A.stride(0), _ptr(sA), sA.stride(0),
+        _ptr(B), B.stride(0), _ptr(sB), sB.stride(0), _ptr(out), code, out.stride(0),
+        _stream(stream))
+    _lib.check("fp8_block_gemm", st)
+    return out
+
+
+def block_gemm_grouped(offsets: torch.Tensor, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor,
+                       sB: torch.Tensor, *, out_dtype=torch.bfloat16, out=None, stream=None):
+    """Grouped per-expert Fprop in one launch.
+
+    offsets: int32 device [G+1]; A [total_M][K]; sA [K/128][>=total_M];
+    B [G][N][K]; sB [G][N/128][K/128].  Returns C [total_M][N].
+    """
+    lib = _lib.load_library()
+    _check_2d("A", A, (torch.uint8, torch.float8_e4m3fn))
+    _check_2d("sA", sA, (torch.float32,))
+    if B.dim() != 3 or not B.is_contiguous() or sB.dim() != 3 or not sB.is_contiguous():
+        raise ValueError("B must be contiguous [G][N][K] and sB contiguous [G][N/128][K/128]")
+    if offsets.dtype != torch.int32 or not offsets.is_cuda:
+        raise TypeError("offsets must be an int32 device tensor")
+    G, N, K = B.shape
+    total_M = A.shape[0]
+    if out is None:
+        out = torch.empty((total_M, N), dtype=out_dtype, device=A.device)
+    code = _lib.OUT_FP32 if out.dtype == torch.float32 else _lib.OUT_BF16
+    st = lib.fp8_block_gemm_grouped(
+        G, _ptr(offsets), total_M, N, K, _ptr(A), A.stride(0), _ptr(sA), sA.stride(0),
+        _ptr(B), B.stride(1), _ptr(sB), _ptr(out), code, out.stride(0), _stream(stream))
+    _lib.check("fp8_block_gemm_grouped", st)
+    return out
+
+
+def amax_history_update(hist: torch.Tensor, amax: torch.Tensor, *, decay: float = 0.9,
+                        init: bool = False, scales_out=None, stream=None):
+    """In-place h <- decay * h + (1 - decay) * amax (or h <- amax when init)."""
+    lib = _lib.load_library()
+    for n, t in (("hist", hist), ("amax", amax)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{n}: contiguous float32 device tensor required")
+    st = lib.fp8_amax_history_update(_ptr(hist), _ptr(amax), hist.numel(), float(decay),
+                                     1 if init else 0, _ptr(scales_out), _stream(stream))
+    _lib.check("fp8_amax_history_update", st)
+    return hist
+
+
+def cast_e4m3(x: torch.Tensor, *, out=None, stream=None):
+    """Saturating round-to-nearest-even FP32 -> E4M3 codes (uint8)."""
+    lib = _lib.load_library()
+    if x.dtype != torch.float32 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x: contiguous float32 device tensor required")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    st = lib.fp8_cast_e4m3(_ptr(x), x.numel(), _ptr(out), _stream(stream))
+    _lib.check("fp8_cast_e4m3", st)
+    return out

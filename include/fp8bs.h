@@ -1,0 +1,211 @@
+/*
+ * fp8bs.h - fine-grained FP8 (E4M3) block-scaled quantization and GEMM for
+ * AMD MI355X (gfx950).  C ABI of libfp8bs.so.
+ *
+ * What the library computes (sources are the pages' titles and sections):
+ *
+ *  - Online activation quantization with one FP32 scale per 1x128 tile of
+ *    contiguous channels of one token ("Fine-Grained Quantization in
+ *    DeepSeek", section 2; "FP8 Mixed Precision: DeepSeek-V3 Training
+ *    Architecture", section 1 item 1; "Introduction to LLM Quantization",
+ *    section 5).
+ *  - Weight quantization with one FP32 scale per 128x128 block ("Fine-Grained
+ *    Quantization in DeepSeek", section 3; "FP8 Mixed Precision", section 1
+ *    item 2 and its block-scale equations).
+ *  - Block-scaled FP8 GEMM: E4M3 products accumulated in FP32, each 128-wide
+ *    K block's partial sum multiplied by its two scales, blocks summed in
+ *    FP32, result rounded once to BF16 (or kept FP32) ("FP8 Mixed Precision",
+ *    section 3 "Decoupled Accumulation in Tensor Core GEMMs"; "Fine-Grained
+ *    Quantization in DeepSeek", section 4; "Introduction to LLM
+ *    Quantization", section 2 steps 1-4), in the forward (Fprop),
+ *    input-gradient (Dgrad) and weight-gradient (Wgrad) layouts
+ *    ("Introduction to LLM Quantization", section 1 items 2-3).
+ *
+ * Quantization rule, per tile (bit-exact, no FMA contraction, no flush of
+ * denormals):
+ *     amax = max |x|                       (x: BF16 widened exactly to FP32)
+ *     s    = max(fl32(amax / 448), fl32(1e-12))
+ *     q    = E4M3(fl32(x / s))             (true IEEE division)
+ *  E4M3 is the 1-4-3 format with bias 7, largest finite 448, no infinities and
+ *  NaN = S.1111.111.  The cast rounds to nearest, ties to even, and saturates
+ *  finite overflow and +-Inf to +-448; a NaN quotient becomes code 0x7F.  A
+ *  tile containing NaN gets scale 0x7FC00000 (canonical NaN) and all-NaN
+ *  codes; a tile containing +-Inf gets scale +Inf.  The stored scale is the
+ *  dequantization multiplier s (x ~ decode(q) * s).
+ *
+ * Conventions for every entry point:
+ *  - All matrices are row-major; ld* are leading dimensions in ELEMENTS.
+ *  - Every pointer except the host-side ones named below is a DEVICE pointer
+ *    allocated by the caller.  The library never allocates, frees or
+ *    synchronizes; it keeps no state beyond per-device properties it caches
+ *    on first use.  Entry points are thread-safe.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued asynchronously on it; faults during execution surface at
+ *    the caller's next synchronization, as in HIP.
+ *  - Arguments are validated on the host before anything is launched; on any
+ *    error nothing is launched and the status says why.  No exceptions cross
+ *    the ABI.
+ *  - Alignment: FP8/BF16/FP32 matrix base pointers must be 16-byte aligned and
+ *    every row start must be 16-byte aligned (ld * element size % 16 == 0);
+ *    scale arrays need 4-byte alignment.
+ *  - Calls that overlap on one stream are ordered; calls on different streams
+ *    that write the same buffers race.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BS_ABI_VERSION 1
+
+typedef enum {
+  FP8_OK = 0,
+  FP8_ERR_NULL = 1,        /* a required pointer is NULL */
+  FP8_ERR_SHAPE = 2,       /* negative size, or a dimension not a multiple of 128 where required */
+  FP8_ERR_LD = 3,          /* leading dimension smaller than the row length */
+  FP8_ERR_ALIGN = 4,       /* pointer or row stride not 16-byte aligned */
+  FP8_ERR_UNSUPPORTED = 5, /* unknown enum value or unsupported combination */
+  FP8_ERR_DEVICE = 6,      /* no current HIP device, or it is not gfx950 */
+  FP8_ERR_LAUNCH = 7,      /* the kernel launch itself failed */
+  FP8_ERR_ALIAS = 8        /* an output buffer overlaps an input buffer */
+} fp8_status;
+
+typedef enum {
+  FP8_TILE_ROW = 0, /* 1x128 tiles along the columns of each row */
+  FP8_TILE_COL = 1  /* 128x1 tiles along the rows of each column; output transposed */
+} fp8_tile_dir;
+
+typedef enum {
+  FP8_LAYOUT_FPROP = 0, /* C[M][N] = A[M][K] . B[N][K]^T,  B = W_q (weights [d_out][d_in]) */
+  FP8_LAYOUT_DGRAD = 1, /* C[M][N] = A[M][K] . B[K][N],    B = W_q stored [d_out = K][d_in = N] */
+  FP8_LAYOUT_WGRAD = 2  /* C[M][N] = A[M][K] . B[N][K]^T,  K = tokens, per-row x per-column scales */
+} fp8_gemm_layout;
+
+typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_FP32 = 1 } fp8_out_dtype;
+
+/*
+ * fp8_quant_act_1x128 - online activation quantization (see the rule above).
+ *
+ *  x          BF16 [rows][ldx >= cols]
+ *  dir        FP8_TILE_ROW: tiles of 1x128 along each row; requires cols % 128 == 0.
+ *               q      [rows][ldq >= cols]            E4M3 codes
+ *               scales [cols/128][ld_s >= rows]       FP32, MN-major: the scales of
+ *                                                     one K block are contiguous
+ *                                                     over rows, matching the
+ *                                                     GEMM's A-scale layout
+ *             FP8_TILE_COL: tiles of 128x1 along each column (weight-gradient
+ *             operands, tiles along tokens); requires rows % 128 == 0.
+ *               q      [cols][ldq >= rows]            transposed codes (K-contiguous
+ *                                                     for the Wgrad GEMM)
+ *               scales [rows/128][ld_s >= cols]       FP32
+ *  scales_in  NULL: online scales from each tile's amax, written to `scales`.
+ *             Otherwise caller-supplied scales (same layout as `scales`; used
+ *             by delayed / history / fixed scale policies): codes are
+ *             E4M3(fl32(x / s_in)) and `scales` is not written (may be NULL).
+ *             ROW direction only.
+ *  amax_out   optional (NULL): per-tile max |x| in the scale layout
+ *             (canonical NaN for tiles containing NaN).
+ *  sat_count  optional (NULL) device uint32 counter, incremented atomically by
+ *             the number of elements the saturating cast clips
+ *             (|fl32(x / s)| > 464, Inf included, NaN not).  The caller zeroes
+ *             it.  Online scales never clip.
+ *  rows == 0 or cols == 0 is a no-op returning FP8_OK.
+ */
+fp8_status fp8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                               fp8_tile_dir dir, uint8_t* q, int64_t ldq,
+                               float* scales, int64_t ld_s, const float* scales_in,
+                               float* amax_out, uint32_t* sat_count, void* stream);
+
+/*
+ * fp8_quant_weight_128x128 - 128x128 weight-block quantization, blocks
+ * anchored at (0, 0); same per-block rule as above over 16384 values.
+ *
+ *  w       BF16 [rows][ldw >= cols]; rows % 128 == 0 and cols % 128 == 0.
+ *  q       E4M3 [rows][ldq >= cols]
+ *  q_t     optional (NULL): the same codes transposed, [cols][ldq_t >= rows]
+ *  scales  FP32 [rows/128][ld_s >= cols/128]
+ */
+fp8_status fp8_quant_weight_128x128(const void* w, int64_t rows, int64_t cols, int64_t ldw,
+                                    uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
+                                    float* scales, int64_t ld_s, void* stream);
+
+/*
+ * fp8_block_gemm - block-scaled FP8 GEMM, FP32 accumulation, per-128-K scale
+ * epilogue:
+ *     C[m][n] = round( sum_kb  sa(m, kb) * sb(n, kb) * sum_{k in kb} A(m, k) * B(k, n) )
+ *  K is always the contraction dimension and K % 128 == 0, K > 0.
+ *
+ *  FP8_LAYOUT_FPROP   (M = tokens, N = d_out, K = d_in)
+ *     A  = X_q  [M][lda >= K];     sA [K/128][ld_sa >= M]     (1x128 row scales)
+ *     B  = W_q  [N][ldb >= K];     sB [N/128][ld_sb >= K/128] (128x128 block scales)
+ *     N % 128 == 0.
+ *  FP8_LAYOUT_DGRAD   (M = tokens, N = d_in, K = d_out)
+ *     A  = dY_q [M][lda >= K];     sA [K/128][ld_sa >= M]     (1x128 row scales)
+ *     B  = W_q  stored [K][ldb >= N] and contracted over its rows (the forward
+ *          weight codes, read transposed in the kernel);
+ *     sB = the same block-scale table, [K/128][ld_sb >= N/128].
+ *     N % 128 == 0.
+ *  FP8_LAYOUT_WGRAD   (M = d_out, N = d_in, K = tokens)
+ *     A  = dY_q^T [M][lda >= K];   sA [K/128][ld_sa >= M]     (128x1 column scales)
+ *     B  = X_q^T  [N][ldb >= K];   sB [K/128][ld_sb >= N]     (128x1 column scales)
+ *  C: [M][ldc >= N], BF16 (round to nearest even) or FP32 (c_dtype).
+ *  M == 0 is a no-op.  C must not overlap A, B or the scales.
+ */
+fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t K,
+                          const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
+                          const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
+                          void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream);
+
+/*
+ * fp8_block_gemm_grouped - one launch of per-expert FPROP GEMMs over row
+ * slices (one GPU's share of a mixture-of-experts FFN layer):
+ *     for g in [0, groups): rows offsets[g] .. offsets[g+1]-1 of A and C use
+ *     expert weights B_g.
+ *  offsets_dev  DEVICE int32 [groups + 1], non-decreasing prefix sums with
+ *               offsets[0] == 0 and offsets[groups] == total_M (the caller
+ *               guarantees this; it is not read on the host).  Empty groups
+ *               are allowed.
+ *  A   X_q [total_M][lda >= K];  sA [K/128][ld_sa >= total_M]
+ *  B   W_q [groups][N][ldb >= K] (group g at B + g * N * ldb)
+ *  sB  [groups][N/128][K/128] contiguous
+ *  C   [total_M][ldc >= N], BF16 or FP32.   N % 128 == 0, K % 128 == 0.
+ */
+fp8_status fp8_block_gemm_grouped(int32_t groups, const int32_t* offsets_dev, int64_t total_M,
+                                  int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                  const float* sA, int64_t ld_sa, const uint8_t* B, int64_t ldb,
+                                  const float* sB, void* C, fp8_out_dtype c_dtype, int64_t ldc,
+                                  void* stream);
+
+/*
+ * fp8_amax_history_update - per-tile state of the exponential amax-history
+ * (delayed) scale policy ("Online Quantization During Training", section 4
+ * and worked example; "Introduction to LLM Quantization", section 5):
+ *     init != 0:  h = amax
+ *     otherwise:  h = fl32(fl32(decay * h) + fl32(fl32(1 - decay) * amax))
+ *     scales_out (optional) = max(fl32(h / 448), fl32(1e-12)), NaN -> 0x7FC00000
+ *  hist, amax, scales_out: FP32 device arrays of n elements.
+ */
+fp8_status fp8_amax_history_update(float* hist, const float* amax, int64_t n, float decay,
+                                   int init, float* scales_out, void* stream);
+
+/*
+ * fp8_cast_e4m3 - the saturating round-to-nearest-even FP32 -> E4M3 cast the
+ * quantizers use, exposed on its own (n elements, any alignment).
+ */
+fp8_status fp8_cast_e4m3(const float* x, int64_t n, uint8_t* q, void* stream);
+
+/* Static string naming a status; never NULL. */
+const char* fp8_status_string(fp8_status s);
+
+/* FP8BS_ABI_VERSION of the built library. */
+int fp8_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

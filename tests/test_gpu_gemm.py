@@ -1,0 +1,217 @@
+"""GPU parity of the block-scaled FP8 GEMMs against the float64 oracle.
+
+Operands are quantized by the ORACLE (so the GEMM check does not depend on
+the GPU quantizers) and uploaded; the GPU result is compared elementwise with
+``tests/tolerance.py``'s bar.  Full-size cases run the whole GEMM in the
+configuration the bench times and compare a seeded sample of output rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as syn
+from oracle import gemm as og
+from oracle import quant
+from tolerance import check_gemm, truncation_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a)
+    if t.dtype == torch.uint16:
+        t = t.view(torch.int16)
+    return t.cuda()
+
+
+def act_scales_dev(s_rows):
+    """oracle [M][K/128] -> device MN-major [K/128][round_up(M, 4)]."""
+    M, KB = s_rows.shape
+    buf = np.zeros((KB, (M + 3) // 4 * 4), np.float32)
+    buf[:, :M] = s_rows.T
+    return dev(buf)
+
+
+def bf16_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_fprop(fp8, Xq, sX, Wq, sW, out_dtype=torch.bfloat16):
+    C = fp8.block_gemm("fprop", dev(Xq), act_scales_dev(sX), dev(Wq), dev(sW), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return C
+
+
+@pytest.mark.parametrize("case", ["toy", "ragged", "lossless", "unit_scale", "fp32_out", "nan_scale"])
+def test_fprop_small(gpu_lib, case):
+    out = "bf16"
+    if case == "toy":
+        xb, wb = syn.toy_layer(0)
+    elif case in ("ragged", "fp32_out", "nan_scale"):
+        xb = syn.activation_with_outliers(333, 640, seed=21)
+        wb = syn.gaussian((384, 640), seed=22, std=0.02)
+    elif case == "lossless":
+        xb, _ = syn.lossless_tiles(200, 384, seed=23, tile=(1, 128), k_range=(-6, 6))
+        wb, _ = syn.lossless_tiles(256, 384, seed=24, tile=(128, 128), k_range=(-6, 6))
+    else:
+        xb = syn.activation_with_outliers(128, 512, seed=25)
+        wb = syn.gaussian((256, 512), seed=26)
+    Xq, sX = quant.quant_rows(xb)
+    Wq, sW = quant.quant_weight(wb)
+    if case == "unit_scale":
+        sX = np.ones_like(sX)
+        sW = np.ones_like(sW)
+    if case == "nan_scale":
+        sX = sX.copy()
+        sX[7, 2] = np.nan
+    R, T = og.fprop(Xq, sX, Wq, sW, with_magnitude=True)
+    E = truncation_bound(Xq, sX, Wq, og.expand_block_scales(sW, Wq.shape[0]))
+    if case == "fp32_out":
+        C = run_fprop(gpu_lib, Xq, sX, Wq, sW, torch.float32)
+        check_gemm(C.cpu().numpy(), R, T, Xq.shape[1], out="fp32", E=E, label=case)
+    else:
+        C = run_fprop(gpu_lib, Xq, sX, Wq, sW)
+        check_gemm(bf16_bits(C), R, T, Xq.shape[1], out=out, E=E, label=case)
+
+
+@pytest.fixture(scope="module")
+def big_layer():
+    """Oracle-quantized X (4096 x 7168, outliers) and W (18432 x 7168)."""
+    xb = syn.activation_with_outliers(4096, 7168, seed=0)
+    wb = syn.gaussian((18432, 7168), seed=1, std=0.02)
+    Xq, sX = quant.quant_rows(xb)
+    del xb
+    Wq, sW = quant.quant_weight(wb)
+    del wb
+    return Xq, sX, Wq, sW
+
+
+def test_fprop_full_size_sampled(gpu_lib, big_layer):
+    Xq, sX, Wq, sW = big_layer
+    C = run_fprop(gpu_lib, Xq, sX, Wq, sW)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 6, replace=False)]))
+    R, T = og.fprop(Xq[rows], sX[rows], Wq, sW, with_magnitude=True)
+    E = truncation_bound(Xq[rows], sX[rows], Wq, og.expand_block_scales(sW, 18432))
+    stats = check_gemm(bf16_bits(C)[rows], R, T, 7168, E=E, label="fprop 4096x18432x7168")
+    assert stats["n"] == rows.size * 18432
+
+
+def test_fprop_deterministic(gpu_lib):
+    xb = syn.activation_with_outliers(512, 1024, seed=27)
+    wb = syn.gaussian((512, 1024), seed=28, std=0.02)
+    Xq, sX = quant.quant_rows(xb)
+    Wq, sW = quant.quant_weight(wb)
+    a = run_fprop(gpu_lib, Xq, sX, Wq, sW)
+    b = run_fprop(gpu_lib, Xq, sX, Wq, sW)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def run_dgrad(fp8, dYq, s_dY, Wq, sW):
+    C = fp8.block_gemm("dgrad", dev(dYq), act_scales_dev(s_dY), dev(Wq), dev(sW))
+    torch.cuda.synchronize()
+    return C
+
+
+def test_dgrad_small_and_layout_identity(gpu_lib):
+    dyb = syn.gaussian((200, 384), seed=31, std=1e-3)          # [tokens][d_out]
+    wb = syn.gaussian((384, 256), seed=32, std=0.02)            # W [d_out][d_in]
+    dYq, s_dY = quant.quant_rows(dyb)
+    Wq, sW = quant.quant_weight(wb)
+    R, T = og.dgrad(dYq, s_dY, Wq, sW, with_magnitude=True)
+    E = truncation_bound(dYq, s_dY, np.ascontiguousarray(Wq.T), og.expand_block_scales(sW.T, 256))
+    C = run_dgrad(gpu_lib, dYq, s_dY, Wq, sW)
+    check_gemm(bf16_bits(C), R, T, 384, E=E, label="dgrad small")
+    # same numbers as Fprop on the explicitly transposed weights
+    F = run_fprop(gpu_lib, dYq, s_dY, np.ascontiguousarray(Wq.T), np.ascontiguousarray(sW.T))
+    assert torch.equal(C.view(torch.int16), F.view(torch.int16))
+
+
+def test_dgrad_full_size_sampled(gpu_lib, big_layer):
+    _, _, Wq, sW = big_layer
+    dyb = syn.gaussian((4096, 18432), seed=4, std=1e-3)
+    dYq, s_dY = quant.quant_rows(dyb)
+    del dyb
+    C = run_dgrad(gpu_lib, dYq, s_dY, Wq, sW)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 4, replace=False)]))
+    R, T = og.dgrad(dYq[rows], s_dY[rows], Wq, sW, with_magnitude=True)
+    E = truncation_bound(dYq[rows], s_dY[rows], np.ascontiguousarray(Wq.T),
+                         og.expand_block_scales(np.ascontiguousarray(sW.T), 7168))
+    check_gemm(bf16_bits(C)[rows], R, T, 18432, E=E, label="dgrad 4096x7168x18432")
+
+
+def run_wgrad(fp8, dYt, s_dy, Xt, s_x, out_dtype=torch.float32):
+    C = fp8.block_gemm("wgrad", dev(dYt), act_scales_dev(s_dy), dev(Xt), act_scales_dev(s_x),
+                       out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return C
+
+
+@pytest.mark.parametrize("out", ["fp32", "bf16"])
+def test_wgrad_small(gpu_lib, out):
+    dyb = syn.gaussian((256, 200), seed=41, std=1e-3)          # [tokens][d_out], ragged d_out
+    xb = syn.activation_with_outliers(256, 136, seed=42)        # [tokens][d_in], ragged d_in
+    dYt, s_dy = quant.quant_cols(dyb)
+    Xt, s_x = quant.quant_cols(xb)
+    R, T = og.wgrad(dYt, s_dy, Xt, s_x, with_magnitude=True)
+    E = truncation_bound(dYt, s_dy, Xt, s_x)
+    C = run_wgrad(gpu_lib, dYt, s_dy, Xt, s_x, torch.float32 if out == "fp32" else torch.bfloat16)
+    y = C.cpu().numpy() if out == "fp32" else bf16_bits(C)
+    check_gemm(y, R, T, 256, out=out, E=E, label=f"wgrad small {out}")
+
+
+def test_wgrad_full_size_sampled(gpu_lib):
+    dyb = syn.gaussian((4096, 18432), seed=4, std=1e-3)
+    xb = syn.activation_with_outliers(4096, 7168, seed=0)
+    dYt, s_dy = quant.quant_cols(dyb)
+    del dyb
+    Xt, s_x = quant.quant_cols(xb)
+    del xb
+    C = run_wgrad(gpu_lib, dYt, s_dy, Xt, s_x)
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 18431], rng.choice(18432, 6, replace=False)]))
+    R, T = og.wgrad(dYt[rows], s_dy[rows], Xt, s_x, with_magnitude=True)
+    E = truncation_bound(dYt[rows], s_dy[rows], Xt, s_x)
+    check_gemm(C.cpu().numpy()[rows], R, T, 4096, out="fp32", E=E, label="wgrad 18432x7168x4096")
+
+
+def run_grouped(fp8, Xq, sX, offsets, Wq_e, sW_e):
+    C = fp8.block_gemm_grouped(dev(offsets.astype(np.int32)), dev(Xq), act_scales_dev(sX),
+                               dev(np.stack(Wq_e)), dev(np.stack(sW_e)))
+    torch.cuda.synchronize()
+    return C
+
+
+def test_grouped_small_with_empty_and_tiny_groups(gpu_lib):
+    counts = np.array([3, 0, 130, 1, 257, 0])
+    off = syn.expert_offsets(counts)
+    xb = syn.activation_with_outliers(int(counts.sum()), 384, seed=51)
+    Xq, sX = quant.quant_rows(xb)
+    ws = [quant.quant_weight(syn.gaussian((256, 384), seed=60 + e, std=0.02)) for e in range(6)]
+    Wq_e, sW_e = [w[0] for w in ws], [w[1] for w in ws]
+    R, T = og.grouped_fprop(Xq, sX, off, Wq_e, sW_e, with_magnitude=True)
+    E = np.concatenate([truncation_bound(Xq[off[e]:off[e + 1]], sX[off[e]:off[e + 1]], Wq_e[e],
+                                         og.expand_block_scales(sW_e[e], 256)) for e in range(6)])
+    C = run_grouped(gpu_lib, Xq, sX, off, Wq_e, sW_e)
+    check_gemm(bf16_bits(C), R, T, 384, E=E, label="grouped small")
+
+
+def test_grouped_full_size_sampled(gpu_lib):
+    counts = syn.expert_counts(16384, 8, seed=0)
+    off = syn.expert_offsets(counts)
+    xb = syn.activation_with_outliers(16384, 7168, seed=0)
+    Xq, sX = quant.quant_rows(xb)
+    del xb
+    ws = [quant.quant_weight(syn.gaussian((2048, 7168), seed=100 + e, std=0.02)) for e in range(8)]
+    Wq_e, sW_e = [w[0] for w in ws], [w[1] for w in ws]
+    C = run_grouped(gpu_lib, Xq, sX, off, Wq_e, sW_e)
+    y = bf16_bits(C)
+    rng = np.random.default_rng(7)
+    for e in range(8):
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = np.unique(np.concatenate([[lo, hi - 1], lo + rng.choice(hi - lo, 2, replace=False)]))
+        R, T = og.fprop(Xq[rows], sX[rows], Wq_e[e], sW_e[e], with_magnitude=True)
+        E = truncation_bound(Xq[rows], sX[rows], Wq_e[e], og.expand_block_scales(sW_e[e], 2048))
+        check_gemm(y[rows], R, T, 7168, E=E, label=f"grouped expert {e}")

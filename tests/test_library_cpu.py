@@ -1,0 +1,163 @@
+"""CPU-side checks of libfp8bs.so: it loads, exports every symbol the header
+declares, and rejects invalid arguments on the host before any launch.  Also
+the exhaustive host proof of the quantizers' division shortcut.  No kernel is
+launched here (there is no GPU in this tier).
+"""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from fine_grained_fp8_amd import _lib, build
+    if not os.path.exists(_lib.LIB_PATH):
+        build.build()
+    return _lib.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_block_gemm",
+                     "fp8_block_gemm_grouped", "fp8_status_string", "fp8_abi_version"):
+        assert required in names
+
+
+def test_exports_every_declared_symbol(lib):
+    from fine_grained_fp8_amd import _lib
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding does not declare {name}"
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                             text=True).stdout
+        exported = set(re.findall(r"\bT (fp8_[a-z0-9_]+)", out))
+        assert set(declared_functions()) <= exported
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.fp8_abi_version() == 1
+    for s in range(9):
+        assert len(lib.fp8_status_string(s)) > 0
+    assert lib.fp8_status_string(99) == b"unknown status"
+
+
+# Fake, well-separated 16-byte-aligned "device" addresses: validation fails
+# before any HIP call, so they are never dereferenced.
+X, Q, S, S2, A, B, C = (0x10000000 * (i + 1) for i in range(7))
+OK, NULL, SHAPE, LD, ALIGN, UNSUP, DEVICE, LAUNCH, ALIAS = range(9)
+
+
+def qa(lib, x=X, rows=64, cols=256, ldx=256, d=0, q=Q, ldq=256, s=S, ld_s=64, s_in=None, amax=None,
+       sat=None):
+    return lib.fp8_quant_act_1x128(x, rows, cols, ldx, d, q, ldq, s, ld_s, s_in, amax, sat, None)
+
+
+def test_quant_act_validation(lib):
+    assert qa(lib, x=None) == NULL
+    assert qa(lib, q=None) == NULL
+    assert qa(lib, s=None) == NULL
+    assert qa(lib, cols=200, ldx=256) == SHAPE
+    assert qa(lib, rows=-1) == SHAPE
+    assert qa(lib, d=7) == UNSUP
+    assert qa(lib, d=1, rows=100) == SHAPE                    # COL needs rows % 128
+    assert qa(lib, d=1, rows=128, s_in=S2) == UNSUP            # caller scales: ROW only
+    assert qa(lib, ldx=128) == LD
+    assert qa(lib, ldq=128) == LD
+    assert qa(lib, ld_s=32) == LD
+    assert qa(lib, x=X + 8) == ALIGN
+    assert qa(lib, ldq=264) == ALIGN
+    assert qa(lib, q=X) == ALIAS
+    assert qa(lib, s=X + 64) == ALIAS
+    assert qa(lib, rows=0, x=None) == OK                       # empty: no-op
+    assert qa(lib, cols=0, x=None) == OK
+
+
+def test_quant_weight_validation(lib):
+    f = lib.fp8_quant_weight_128x128
+    assert f(X, 256, 256, 256, Q, 256, None, 0, S, 2, None) in (DEVICE, OK)
+    assert f(X, 200, 256, 256, Q, 256, None, 0, S, 2, None) == SHAPE
+    assert f(None, 256, 256, 256, Q, 256, None, 0, S, 2, None) == NULL
+    assert f(X, 256, 256, 256, Q, 256, A, 128, S, 2, None) == LD
+    assert f(X, 256, 256, 256, Q, 256, None, 0, S, 1, None) == LD
+    assert f(X, 256, 256, 256, X + 1024, 256, None, 0, S, 2, None) == ALIAS
+
+
+def gemm(lib, layout=0, M=256, N=256, K=512, a=A, lda=512, sa=S, ld_sa=256, b=B, ldb=512, sb=S2,
+         ld_sb=4, c=C, dt=0, ldc=256):
+    return lib.fp8_block_gemm(layout, M, N, K, a, lda, sa, ld_sa, b, ldb, sb, ld_sb, c, dt, ldc, None)
+
+
+def test_gemm_validation(lib):
+    assert gemm(lib, layout=3) == UNSUP
+    assert gemm(lib, dt=5) == UNSUP
+    assert gemm(lib, K=200, lda=256) == SHAPE
+    assert gemm(lib, K=0) == SHAPE
+    assert gemm(lib, N=200, ldc=256) == SHAPE                 # FPROP weights need N % 128
+    assert gemm(lib, M=0, a=None) == OK
+    assert gemm(lib, a=None) == NULL
+    assert gemm(lib, lda=256) == LD
+    assert gemm(lib, ld_sa=100) == LD
+    assert gemm(lib, ld_sb=2) == LD
+    assert gemm(lib, c=C + 4) == ALIGN
+    assert gemm(lib, ldc=260) == ALIGN                        # bf16 row stride not 16-byte aligned
+    assert gemm(lib, c=A + 4096) == ALIAS
+    # DGRAD: B stored [K][N], block scales [K/128][N/128]
+    assert gemm(lib, layout=1, ldb=128, ld_sb=2) == LD
+    assert gemm(lib, layout=1, ldb=256, ld_sb=1) == LD
+    # WGRAD: any N, column scales [K/128][N]
+    assert gemm(lib, layout=2, N=200, ldc=208, ld_sb=150) == LD
+    assert gemm(lib, layout=2, N=200, ldc=208, ld_sb=200, dt=1) in (DEVICE, OK)
+
+
+def test_grouped_validation(lib):
+    f = lib.fp8_block_gemm_grouped
+    args = [8, X, 1024, 256, 512, A, 512, S, 1024, B, 512, S2, C, 0, 256, None]
+    assert f(*args) in (DEVICE, OK)
+    bad = list(args); bad[0] = 0
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[1] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[3] = 200
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[10] = 256
+    assert f(*bad) == LD
+
+
+def test_no_device_reported_without_gpu(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert qa(lib) == DEVICE
+    assert gemm(lib) == DEVICE
+    assert lib.fp8_cast_e4m3(X, 16, Q, None) == DEVICE
+
+
+def test_division_shortcut_exhaustive(tmp_path):
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    exe = str(tmp_path / "check_div")
+    src = os.path.join(ROOT, "tests", "c", "check_div.c")
+    flags = ["-O2", "-ffp-contract=off", "-fopenmp"]
+    if "fma" in open("/proc/cpuinfo").read():
+        flags.append("-mfma")
+    subprocess.run([gcc, *flags, "-o", exe, src, "-lm"], check=True)
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stdout
+    assert "mismatches=0" in res.stdout
+    assert "pairs=1065402240" in res.stdout

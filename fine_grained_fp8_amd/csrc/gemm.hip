@@ -23,17 +23,20 @@
 //    token-side operand the MFMA "B" (columns = output rows m): each lane owns
 //    4 consecutive n of one output row m (contiguous stores), and in
 //    Fprop/Dgrad one weight-block scale per wave and K block.
-//  * Workgroup tile 256 (n) x 256 (m) x 128 (k), eight wave64s.  Operand tiles
-//    are staged in LDS in a 16-byte-chunk XOR swizzle (conflict-free for the
-//    MFMA operand reads and for the transposing Dgrad stores) with two stages:
-//    K block kb+1 streams into one stage while block kb is multiplied out of
-//    the other; one barrier per K block.
-//  * K-contiguous operands are loaded straight into LDS with
-//    buffer_load_dwordx4 ... lds (no staging registers); the buffer range ends
-//    at the last valid row, so ragged M/N tails read zeros.  Dgrad reads the
-//    forward weight codes W_q [d_out][d_in] transposed: each thread loads
-//    16 rows x 4 bytes, transposes 4x4 byte blocks with v_perm_b32 and writes
-//    16-byte K-contiguous chunks.
+//  * Workgroup tile 256 (n) x 128 (m) x 128 (k): four wave64s, one per SIMD,
+//    each 128 x 64 with the full 512-register budget (accumulators in VGPRs,
+//    operands free to live in AGPRs).
+//  * Three LDS stages, each tile of each stage its own LDS object (so the
+//    compiler sees that the DMA into one stage never aliases reads of
+//    another): K blocks kb+1 and kb+2 stream in by DMA (buffer_load_dwordx4
+//    ... lds, no staging registers) while block kb is multiplied; one barrier
+//    per K block.  The buffer range ends at the last valid row, so ragged M/N
+//    tails read zeros.  Tiles store 16-byte chunks XOR-swizzled by row & 7
+//    (conflict-free MFMA operand reads).  The scales of each K block
+//    (contiguous in the MN-major layout) ride along in the same stage.
+//  * Dgrad reads the forward weight codes W_q [d_out][d_in] transposed: the
+//    tile is DMA'd as stored ([k][n]) and ds_read_b64_tr_b8 transposes it on
+//    the way into the MFMA operand registers.
 //  * Workgroup ids are remapped so each XCD (ids congruent mod 8) walks a
 //    contiguous, M-grouped run of tiles and its private L2 sees the reuse.
 #include "device.hpp"
@@ -43,20 +46,22 @@ namespace fp8bs {
 
 namespace {
 
-constexpr int BM = 256;        // token rows per workgroup
+constexpr int BM = 128;        // token rows per workgroup
 constexpr int BN = 256;        // output columns per workgroup
 constexpr int BK = 128;        // one scale block
-constexpr int kThreads = 512;
-constexpr int kTileBytes = 256 * BK;
-constexpr int kStageBytes = 2 * kTileBytes + 2048;   // W tile, X tile, 2 x 256 scales
-constexpr int kGroupM = 4;
+constexpr int kThreads = 256;
+constexpr int kWTile = BN * BK;   // 32 KB
+constexpr int kXTile = BM * BK;   // 16 KB
+constexpr int kScaleBytes = 2048; // token scales [256] + weight-side scales [256]
+constexpr int kGroupM = 8;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// Wave tile: 128 output columns (n) x 64 output rows (m); waves 2 (n) x 2 (m).
+constexpr int WN = 128, WM = 64, NI = WN / 16, NJ = WM / 16;
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t total) {
   // ids congruent mod 8 share an XCD; give each XCD a contiguous run of tiles
@@ -76,32 +81,57 @@ __device__ __forceinline__ void grouped_order(int64_t t, int64_t tiles_m, int64_
   tn = r / gsz;
 }
 
-__device__ __forceinline__ v8i read_operand(const uint8_t* tile, int row, int g) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(tile + swz(row, 2 * g));
-  const uint4 hi = *reinterpret_cast<const uint4*>(tile + swz(row, 2 * g + 1));
-  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+__device__ __forceinline__ v8i pair(const uint8_t* lo_p, const uint8_t* hi_p) {
+  const v4i lo = *reinterpret_cast<const v4i*>(lo_p);
+  const v4i hi = *reinterpret_cast<const v4i*>(hi_p);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Wave tile: WN output columns x WM output rows.  Wgrad uses 64 x 128 (fewer
-// distinct per-column weight scales per lane), the others 128 x 64.
-template <int kLayout>
-struct WaveShape {
-  static constexpr int WN = kLayout == kWgrad ? 64 : 128;
-  static constexpr int WM = kLayout == kWgrad ? 128 : 64;
-  static constexpr int NI = WN / 16;
-  static constexpr int NJ = WM / 16;
-  static constexpr int WAVES_N = BN / WN;
-};
+// Dgrad weight tile kept as stored, [128 k][256 n] bytes, 16-byte chunks of a
+// row XOR-swizzled by k & 7.  ds_read_b64_tr_b8 turns it into MFMA "A"
+// operands: within each 16-lane group, lane r names row M[r] (8 bytes) and
+// output lane j receives byte b of M[2b + (j >> 3)][j & 7].  Pointing even
+// lanes at (k0 + r/2, n..n+7) and odd lanes at (k0 + r/2, n+8..n+15) gives
+// lane j the 8 consecutive k of column n + j - the same k order as the
+// K-contiguous operands.
+__device__ __forceinline__ v8i read_operand_t(const uint8_t* tile, int n_sub, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int c16 = n_sub >> 4;
+  v8i out;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int k = g * 32 + t * 8 + (j >> 1);
+    const uint8_t* src = tile + k * 256 + ((c16 ^ (k & 7)) << 4) + 8 * (j & 1);
+    const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(src));
+    out[2 * t] = r[0];
+    out[2 * t + 1] = r[1];
+  }
+  return out;
+}
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
+// operations of this wave are outstanding and all LDS/scalar ones are done.
+template <int vm>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(vm >= 0 && vm < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14));
+}
 
 template <int kLayout, bool kOutF32, bool kGrouped>
-__global__ __launch_bounds__(kThreads, 2) void block_gemm_kernel(GemmProblem p, int64_t total_tiles) {
-  using S = WaveShape<kLayout>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
+__global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, int64_t total_tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_w0[kWTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_w1[kWTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_w2[kWTile];
+  // X-tile objects carry the stage's scale vectors after the codes (fewer
+  // distinct DMA targets for the compiler's wait tracking)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_x0[kXTile + kScaleBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_x1[kXTile + kScaleBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_x2[kXTile + kScaleBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave % S::WAVES_N, wm = wave / S::WAVES_N;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
   const int64_t tiles_n = (p.N + BN - 1) / BN;
 
   // ---- tile coordinates ----
@@ -150,145 +180,166 @@ __global__ __launch_bounds__(kThreads, 2) void block_gemm_kernel(GemmProblem p, 
     rsrc_w = __builtin_amdgcn_make_buffer_rsrc((void*)(Bp + n0 * p.ldb), (short)0,
                                                rows_n * (int)p.ldb, (int)kRsrcWord3);
   }
-  // this lane's slot in each of the wave's 4 load instructions (8 rows x 128 B each)
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);      // wave-uniform (SGPR)
-  const int lrow8 = wave * 32 + (lane >> 3);
-  const int lslot = lane & 7;
-  const int cq = tid & 63, kg = tid >> 6;      // Dgrad: columns 4cq.., k rows 16kg..
-  uint32_t rwt[16];
+  // Per-lane byte offsets of the wave's DMA instructions (1 KB each: 8 rows of
+  // a K-contiguous tile, or 4 k-rows of the Dgrad tile).  With the row & 7
+  // swizzle a lane's chunk is the same in every instruction, so instructions
+  // differ by a uniform row stride.  The whole offset goes into the per-lane
+  // VGPR offset, which is what the buffer range check applies to.
+  const int xrow = wave * 32 + (lane >> 3);                          // + 8 j, j < 4
+  const uint32_t off_x = (uint32_t)(xrow * (int)p.lda + (((lane & 7) ^ (lane >> 3)) << 4));
+  uint32_t off_w, off_w_odd = 0;
+  if constexpr (kLayout == kDgrad) {
+    const int k = wave * 32 + (lane >> 4);                           // + 4 j, j < 8
+    off_w = (uint32_t)(k * (int)p.ldb + (((lane & 15) ^ (k & 7)) << 4));
+    off_w_odd = (uint32_t)(k * (int)p.ldb + (((lane & 15) ^ ((k + 4) & 7)) << 4));
+  } else {
+    const int wrow = wave * 64 + (lane >> 3);                        // + 8 j, j < 8
+    off_w = (uint32_t)(wrow * (int)p.ldb + (((lane & 7) ^ (lane >> 3)) << 4));
+  }
+  const int w_kstride = kLayout == kDgrad ? BK * (int)p.ldb : BK;   // bytes per K block
+  const int w_jstride = kLayout == kDgrad ? 4 * (int)p.ldb : 8 * (int)p.ldb;
 
-  auto issue_loads = [&](int kb, int stage) {
-    uint8_t* st = smem + stage * kStageBytes;
-    const int soff = kb * BK;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = lrow8 + j * 8;
-      const int lc = lslot ^ ((row ^ (row >> 3)) & 7);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_x, (lds_ptr_t)(st + kTileBytes + (wave_u * 32 + j * 8) * 128),
-                                               16, (uint32_t)(row * (int)p.lda + lc * 16), soff, 0, 0);
-    }
-    if constexpr (kLayout == kDgrad) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        rwt[i] = __builtin_amdgcn_raw_buffer_load_b32(
-            rsrc_w, (uint32_t)((kb * BK + kg * 16 + i) * (int)p.ldb + cq * 4), 0, 0);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = lrow8 + j * 8;
-        const int lc = lslot ^ ((row ^ (row >> 3)) & 7);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w, (lds_ptr_t)(st + (wave_u * 32 + j * 8) * 128),
-                                                 16, (uint32_t)(row * (int)p.ldb + lc * 16), soff, 0, 0);
-      }
-    }
-    // token-side scales of this K block, rows m0..m0+255 (contiguous in the MN-major layout)
-    if (wave_u == 0) {
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.sA + (int64_t)kb * p.ld_sa + m0), (short)0, rows_m * 4, (int)kRsrcWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + 2 * kTileBytes), 16,
-                                               (uint32_t)(lane * 16), 0, 0, 0);
-    }
-    if constexpr (kLayout == kWgrad) {
-      if (wave_u == 1) {
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(sBp + (int64_t)kb * p.ld_sb + n0), (short)0, rows_n * 4, (int)kRsrcWord3);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + 2 * kTileBytes + 1024), 16,
-                                                 (uint32_t)(lane * 16), 0, 0, 0);
-      }
-    }
-  };
-  auto store_dgrad_w = [&](int stage) {
-    uint8_t* st = smem + stage * kStageBytes;
-    uint32_t o[4][4];
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd)
-      transpose4x4_bytes(rwt[4 * qd], rwt[4 * qd + 1], rwt[4 * qd + 2], rwt[4 * qd + 3],
-                         o[qd][0], o[qd][1], o[qd][2], o[qd][3]);
+  // weight-block scales (Fprop / Dgrad), read through a range-checked buffer
+  const int64_t nb0 = n0 / 128;
+  const int nb_valid = (int)((p.N / 128 - nb0) < 2 ? (p.N / 128 - nb0) : 2);
+  const int64_t sw_elems = kLayout == kFprop ? (p.N / 128) * p.ld_sb : (p.K / BK) * p.ld_sb;
+  const __amdgpu_buffer_rsrc_t rsrc_sw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)sBp, (short)0, kLayout == kWgrad ? 0 : (int)(sw_elems * 4), (int)kRsrcWord3);
+
+  // Every wave issues the same number of DMA instructions per K block (the
+  // scale vectors are loaded by all four waves; they write identical bytes),
+  // so one vmcnt threshold fits every wave.
+  constexpr int kOpsPerBlock = 4 + 8 + 1 + 1;
+  auto issue_loads = [&](int kb, uint8_t* wst, uint8_t* xst) {
+    float* sst = reinterpret_cast<float*>(xst + kXTile);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(st + swz(cq * 4 + j, kg)) = make_uint4(o[0][j], o[1][j], o[2][j], o[3][j]);
-  };
-
-  // weight-block scale (Fprop / Dgrad): one value per wave and K block
-  const int nblk_last = (int)(p.N / 128) - 1;
-  int wblk = (int)((n0 + wn * S::WN) / 128);
-  wblk = wblk < nblk_last ? wblk : nblk_last;
-  auto weight_scale = [&](int kb) -> float {
-    if constexpr (kLayout == kFprop) return sBp[(int64_t)wblk * p.ld_sb + kb];
-    else if constexpr (kLayout == kDgrad) return sBp[(int64_t)kb * p.ld_sb + wblk];
-    else return 0.f;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_x, (lds_ptr_t)(xst + (wave * 4 + j) * 1024), 16,
+                                               off_x + (uint32_t)(kb * BK + j * 8 * (int)p.lda), 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t ow = (kLayout == kDgrad && (j & 1)) ? off_w_odd : off_w;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w, (lds_ptr_t)(wst + (wave * 8 + j) * 1024), 16,
+                                               ow + (uint32_t)(kb * w_kstride + j * w_jstride), 0, 0, 0);
+    }
+    // token-side scales of this K block, rows m0..m0+127 (contiguous in the MN-major layout)
+    {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.sA + (int64_t)kb * p.ld_sa + m0), (short)0, rows_m * 4, (int)kRsrcWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sst), 16, (uint32_t)(lane * 16), 0, 0, 0);
+    }
+    if constexpr (kLayout == kWgrad) {
+      // per-column weight-side scales of this K block, columns n0..n0+255
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(sBp + (int64_t)kb * p.ld_sb + n0), (short)0, rows_n * 4, (int)kRsrcWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sst + 256), 16, (uint32_t)(lane * 16), 0, 0, 0);
+    } else {
+      // the two weight-block scales of this K block (n-blocks n0/128 and
+      // n0/128 + 1): lanes 0 and 1 fetch one float each into sst[256..257]
+      const uint32_t idx = kLayout == kFprop ? (uint32_t)((nb0 + lane) * p.ld_sb + kb)
+                                             : (uint32_t)(kb * p.ld_sb + nb0 + lane);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_sw, (lds_ptr_t)(sst + 256), 4,
+                                               lane < nb_valid ? idx * 4u : 0xFFFFFFF0u, 0, 0, 0);
+    }
   };
 
   const int lrow = lane & 15, lgrp = lane >> 4;
-  v4f acc[S::NI][S::NJ];
-#pragma unroll
-  for (int i = 0; i < S::NI; ++i)
-#pragma unroll
-    for (int j = 0; j < S::NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // swizzled LDS addresses of this lane's operand rows: row & 7 == lrow & 7 for
+  // every subtile, so subtile j (i) sits a constant 2048 B further on
+  const int sw = lrow & 7;
+  const int x_lo = (wm * WM + lrow) * 128 + (((2 * lgrp) ^ sw) << 4);
+  const int x_hi = (wm * WM + lrow) * 128 + (((2 * lgrp + 1) ^ sw) << 4);
+  const int w_lo = (wn * WN + lrow) * 128 + (((2 * lgrp) ^ sw) << 4);
+  const int w_hi = (wn * WN + lrow) * 128 + (((2 * lgrp + 1) ^ sw) << 4);
 
-  float wsc = weight_scale(0);
-  issue_loads(0, 0);
-  if constexpr (kLayout == kDgrad) store_dgrad_w(0);
+  v4f acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb = 0; kb < KB; ++kb) {
-    const int stage = kb & 1;
-    __builtin_amdgcn_s_waitcnt(0);           // this wave's loads for block kb have landed
-    __syncthreads();                         // ... and every other wave's; stage kb^1 is free
-    const bool more = kb + 1 < KB;
-    float wsc_next = 0.f;
-    if (more) {
-      wsc_next = weight_scale(kb + 1);
-      issue_loads(kb + 1, stage ^ 1);
-    }
-    const uint8_t* wt = smem + stage * kStageBytes;
-    const uint8_t* xt = wt + kTileBytes;
-    const float* sxl = reinterpret_cast<const float*>(wt + 2 * kTileBytes);
+  // ---- one K block out of stage (wt, xt, sxl); block kb+2 streams into (wnx, xnx, snx) ----
+  auto step = [&](int kb, const uint8_t* wt, const uint8_t* xt, uint8_t* wnx, uint8_t* xnx) {
+    const float* sxl = reinterpret_cast<const float*>(xt + kXTile);
+    if (kb + 1 < KB) wait_vm_lgkm0<kOpsPerBlock>();   // block kb landed; kb+1 may still fly
+    else wait_vm_lgkm0<0>();
+    // Bare barrier: __syncthreads() would add a release fence, i.e. a full
+    // vmcnt(0) drain of the DMA still in flight for later blocks.  The waits
+    // above already make this wave's block-kb data visible; the empty asm
+    // keeps the compiler from moving LDS accesses across the barrier.
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+
+    // All LDS reads of this block first, then the DMA for block kb+2: no LDS
+    // read follows a DMA issue inside a step, so the compiler never has to
+    // guess whether they alias (it would drain the DMA with vmcnt(0)).
     const float* swl = sxl + 256;
-
-    v8i bx[S::NJ];
-    float c[S::NJ];
+    float wsc = 0.f;
+    if constexpr (kLayout != kWgrad) wsc = swl[(int)((n0 + wn * WN) / 128 - nb0)];
+    v8i bx[NJ];
+    float c[NJ];
 #pragma unroll
-    for (int j = 0; j < S::NJ; ++j) {
-      const int r = wm * S::WM + j * 16 + lrow;
-      bx[j] = read_operand(xt, r, lgrp);
-      c[j] = kLayout == kWgrad ? sxl[r] : sxl[r] * wsc;
+    for (int j = 0; j < NJ; ++j) {
+      bx[j] = pair(xt + x_lo + j * 2048, xt + x_hi + j * 2048);
+      const float t = sxl[wm * WM + j * 16 + lrow];
+      c[j] = kLayout == kWgrad ? t : t * wsc;
     }
+    v8i a[NI];
 #pragma unroll
-    for (int i = 0; i < S::NI; ++i) {
-      const v8i a = read_operand(wt, wn * S::WN + i * 16 + lrow, lgrp);
-      float4 rs = make_float4(0.f, 0.f, 0.f, 0.f);
-      if constexpr (kLayout == kWgrad)
-        rs = *reinterpret_cast<const float4*>(swl + wn * S::WN + i * 16 + lgrp * 4);
+    for (int i = 0; i < NI; ++i) {
+      if constexpr (kLayout == kDgrad) a[i] = read_operand_t(wt, wn * WN + i * 16, lane);
+      else a[i] = pair(wt + w_lo + i * 2048, wt + w_hi + i * 2048);
+    }
+    float4 rs[NI];
+    if constexpr (kLayout == kWgrad) {
 #pragma unroll
-      for (int j = 0; j < S::NJ; ++j) {
+      for (int i = 0; i < NI; ++i) rs[i] = *reinterpret_cast<const float4*>(swl + wn * WN + i * 16 + lgrp * 4);
+    }
+    __asm__ volatile("" ::: "memory");
+    if (kb + 2 < KB) issue_loads(kb + 2, wnx, xnx);
+
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      v4f P[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
-        const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bx[j], zero, 0, 0,
-                                                                      0, 127, 0, 127);
-        if constexpr (kLayout == kWgrad) {
-          acc[i][j][0] = __builtin_fmaf(P[0] * rs.x, c[j], acc[i][j][0]);
-          acc[i][j][1] = __builtin_fmaf(P[1] * rs.y, c[j], acc[i][j][1]);
-          acc[i][j][2] = __builtin_fmaf(P[2] * rs.z, c[j], acc[i][j][2]);
-          acc[i][j][3] = __builtin_fmaf(P[3] * rs.w, c[j], acc[i][j][3]);
-        } else {
+        P[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bx[j], zero, 0, 0, 0, 127, 0, 127);
+      }
+      if constexpr (kLayout == kWgrad) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(P[v], c[j], acc[i][j][v]);
+        for (int j = 0; j < NJ; ++j) {
+          acc[i][j][0] = __builtin_fmaf(P[j][0] * rs[i].x, c[j], acc[i][j][0]);
+          acc[i][j][1] = __builtin_fmaf(P[j][1] * rs[i].y, c[j], acc[i][j][1]);
+          acc[i][j][2] = __builtin_fmaf(P[j][2] * rs[i].z, c[j], acc[i][j][2]);
+          acc[i][j][3] = __builtin_fmaf(P[j][3] * rs[i].w, c[j], acc[i][j][3]);
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(P[j][v], c[j], acc[i][j][v]);
       }
     }
-    if (more) {
-      if constexpr (kLayout == kDgrad) store_dgrad_w(stage ^ 1);
-      wsc = wsc_next;
-    }
+  };
+
+  issue_loads(0, lds_w0, lds_x0);
+  if (KB > 1) issue_loads(1, lds_w1, lds_x1);
+  for (int kb = 0; kb < KB; kb += 3) {
+    step(kb, lds_w0, lds_x0, lds_w2, lds_x2);
+    if (kb + 1 < KB) step(kb + 1, lds_w1, lds_x1, lds_w0, lds_x0);
+    if (kb + 2 < KB) step(kb + 2, lds_w2, lds_x2, lds_w1, lds_x1);
   }
 
   // ---- epilogue: round and store ----
 #pragma unroll
-  for (int j = 0; j < S::NJ; ++j) {
-    const int64_t m = m0 + wm * S::WM + j * 16 + lrow;
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t m = m0 + wm * WM + j * 16 + lrow;
     if (m >= m_end) continue;
 #pragma unroll
-    for (int i = 0; i < S::NI; ++i) {
-      const int64_t n = n0 + wn * S::WN + i * 16 + lgrp * 4;
+    for (int i = 0; i < NI; ++i) {
+      const int64_t n = n0 + wn * WN + i * 16 + lgrp * 4;
       if (n >= p.N) continue;
       const v4f r = acc[i][j];
       if constexpr (kOutF32) {

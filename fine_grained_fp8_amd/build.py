@@ -4,7 +4,8 @@
 
 Every call recompiles.  Flags that matter for the numerics: FP contraction
 off (every rounding is the one written), FP32 denormals kept, correctly
-rounded FP32 division, and no packed-FP32 instructions.
+rounded FP32 division, and no packed-FP32 instructions.  For speed: MFMA
+results are kept in VGPRs.
 """
 from __future__ import annotations
 
@@ -31,6 +32,9 @@ HIPCC_FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results (the per-K-block partial sums) in VGPRs, where the FP32
+    # scale fold reads them, instead of AGPRs plus a copy per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -299,14 +299,9 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
     __asm__ volatile("" ::: "memory");
     if (kb + 2 < KB) issue_loads(kb + 2, wnx, xnx);
 
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      v4f P[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const v4f zero = {0.f, 0.f, 0.f, 0.f};
-        P[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bx[j], zero, 0, 0, 0, 127, 0, 127);
-      }
+    // Software pipeline: the MFMAs of subtile row i are issued before the FP32
+    // folds of row i-1, so the matrix core runs while the VALU folds.
+    auto fold = [&](int i, const v4f (&P)[NJ]) {
       if constexpr (kLayout == kWgrad) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -321,7 +316,26 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(P[j][v], c[j], acc[i][j][v]);
       }
+    };
+    v4f P0[NJ], P1[NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      v4f (&Pc)[NJ] = (i & 1) ? P1 : P0;
+      // operands in AGPRs (the MFMA reads them there), leaving the VGPRs to
+      // the accumulators and the partial sums the VALU folds
+      __asm__ volatile("" : "+a"(a[i]));
+      if (i == 0) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) __asm__ volatile("" : "+a"(bx[j]));
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+        Pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bx[j], zero, 0, 0, 0, 127, 0, 127);
+      }
+      if (i > 0) fold(i - 1, (i & 1) ? P0 : P1);
     }
+    fold(NI - 1, ((NI - 1) & 1) ? P1 : P0);
   };
 
   issue_loads(0, lds_w0, lds_x0);

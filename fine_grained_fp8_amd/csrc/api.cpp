@@ -185,7 +185,8 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
   if (ldb % 16 != 0) return FP8_ERR_ALIGN;
   if (ldb > (int64_t{1} << 23)) return FP8_ERR_UNSUPPORTED;
   if (layout == FP8_LAYOUT_DGRAD && K * ldb >= (int64_t{1} << 31)) return FP8_ERR_UNSUPPORTED;
-  if (layout != FP8_LAYOUT_WGRAD && sb_rows * ld_sb >= (int64_t{1} << 31)) return FP8_ERR_UNSUPPORTED;
+  // the weight-block scales are read through a buffer whose byte range is 32-bit
+  if (layout != FP8_LAYOUT_WGRAD && sb_rows * ld_sb >= (int64_t{1} << 29)) return FP8_ERR_UNSUPPORTED;
   const int64_t esz = c_dtype == FP8_OUT_FP32 ? 4 : 2;
   const Range rc = span(C, M, N * esz, ldc * esz);
   if (overlap(rc, span(A, M, K, lda)) || overlap(rc, span(B, b_rows, b_cols, ldb)) ||
@@ -218,6 +219,7 @@ fp8_status fp8_block_gemm_grouped(int32_t groups, const int32_t* offsets_dev, in
   if (ldb < K) return FP8_ERR_LD;
   if (ldb % 16 != 0) return FP8_ERR_ALIGN;
   if (ldb > (int64_t{1} << 23)) return FP8_ERR_UNSUPPORTED;
+  if ((N / 128) * (K / 128) >= (int64_t{1} << 29)) return FP8_ERR_UNSUPPORTED;
   const int64_t esz = c_dtype == FP8_OUT_FP32 ? 4 : 2;
   const Range rc = span(C, total_M, N * esz, ldc * esz);
   if (overlap(rc, span(A, total_M, K, lda)) ||

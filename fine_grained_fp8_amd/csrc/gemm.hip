@@ -201,46 +201,52 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
 
   // weight-block scales (Fprop / Dgrad), read through a range-checked buffer
   const int64_t nb0 = n0 / 128;
-  const int nb_valid = (int)((p.N / 128 - nb0) < 2 ? (p.N / 128 - nb0) : 2);
+  // Lanes 0 and 1 fetch the scales of n-blocks nb0 and nb0 + 1 (every other
+  // lane repeats block nb0 + 2).  A block past the last one lies past the end
+  // of the buffer, so the range check returns zero for it - no branch needed.
+  const uint32_t sw_lane = (uint32_t)(nb0 + (lane < 2 ? lane : 2));
+  const uint32_t sw_off = kLayout == kFprop ? sw_lane * (uint32_t)p.ld_sb * 4u : sw_lane * 4u;
+  const uint32_t sw_kstride = kLayout == kFprop ? 4u : (uint32_t)p.ld_sb * 4u;
   const int64_t sw_elems = kLayout == kFprop ? (p.N / 128) * p.ld_sb : (p.K / BK) * p.ld_sb;
   const __amdgpu_buffer_rsrc_t rsrc_sw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)sBp, (short)0, kLayout == kWgrad ? 0 : (int)(sw_elems * 4), (int)kRsrcWord3);
 
   // Every wave issues the same number of DMA instructions per K block (the
   // scale vectors are loaded by all four waves; they write identical bytes),
-  // so one vmcnt threshold fits every wave.
+  // so one vmcnt threshold fits every wave.  issue_load(kb, op, ...) issues
+  // DMA instruction `op` of block kb: 0-3 token rows, 4-11 weight rows, 12
+  // the token-side scales, 13 the weight-side scales.
   constexpr int kOpsPerBlock = 4 + 8 + 1 + 1;
-  auto issue_loads = [&](int kb, uint8_t* wst, uint8_t* xst) {
+  auto issue_load = [&](int kb, int op, uint8_t* wst, uint8_t* xst) {
     float* sst = reinterpret_cast<float*>(xst + kXTile);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_x, (lds_ptr_t)(xst + (wave * 4 + j) * 1024), 16,
-                                               off_x + (uint32_t)(kb * BK + j * 8 * (int)p.lda), 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    if (op < 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_x, (lds_ptr_t)(xst + (wave * 4 + op) * 1024), 16,
+                                               off_x + (uint32_t)(kb * BK + op * 8 * (int)p.lda), 0, 0, 0);
+    } else if (op < 12) {
+      const int j = op - 4;
       const uint32_t ow = (kLayout == kDgrad && (j & 1)) ? off_w_odd : off_w;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w, (lds_ptr_t)(wst + (wave * 8 + j) * 1024), 16,
                                                ow + (uint32_t)(kb * w_kstride + j * w_jstride), 0, 0, 0);
-    }
-    // token-side scales of this K block, rows m0..m0+127 (contiguous in the MN-major layout)
-    {
+    } else if (op == 12) {
+      // token-side scales of this K block, rows m0..m0+127 (contiguous in the MN-major layout)
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.sA + (int64_t)kb * p.ld_sa + m0), (short)0, rows_m * 4, (int)kRsrcWord3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sst), 16, (uint32_t)(lane * 16), 0, 0, 0);
-    }
-    if constexpr (kLayout == kWgrad) {
+    } else if constexpr (kLayout == kWgrad) {
       // per-column weight-side scales of this K block, columns n0..n0+255
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(sBp + (int64_t)kb * p.ld_sb + n0), (short)0, rows_n * 4, (int)kRsrcWord3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sst + 256), 16, (uint32_t)(lane * 16), 0, 0, 0);
     } else {
       // the two weight-block scales of this K block (n-blocks n0/128 and
-      // n0/128 + 1): lanes 0 and 1 fetch one float each into sst[256..257]
-      const uint32_t idx = kLayout == kFprop ? (uint32_t)((nb0 + lane) * p.ld_sb + kb)
-                                             : (uint32_t)(kb * p.ld_sb + nb0 + lane);
+      // n0/128 + 1) land in sst[256..257]
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_sw, (lds_ptr_t)(sst + 256), 4,
-                                               lane < nb_valid ? idx * 4u : 0xFFFFFFF0u, 0, 0, 0);
+                                               sw_off + (uint32_t)kb * sw_kstride, 0, 0, 0);
     }
+  };
+  auto issue_loads = [&](int kb, uint8_t* wst, uint8_t* xst) {
+#pragma unroll
+    for (int op = 0; op < kOpsPerBlock; ++op) issue_load(kb, op, wst, xst);
   };
 
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -261,15 +267,19 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
   // ---- one K block out of stage (wt, xt, sxl); block kb+2 streams into (wnx, xnx, snx) ----
   auto step = [&](int kb, const uint8_t* wt, const uint8_t* xt, uint8_t* wnx, uint8_t* xnx) {
     const float* sxl = reinterpret_cast<const float*>(xt + kXTile);
-    if (kb + 1 < KB) wait_vm_lgkm0<kOpsPerBlock>();   // block kb landed; kb+1 may still fly
-    else wait_vm_lgkm0<0>();
+    wait_vm_lgkm0<kOpsPerBlock>();   // block kb landed; the next block may still fly
+    const bool live = kb < KB;        // false for the padding steps
     // Bare barrier: __syncthreads() would add a release fence, i.e. a full
     // vmcnt(0) drain of the DMA still in flight for later blocks.  The waits
     // above already make this wave's block-kb data visible; the empty asm
     // keeps the compiler from moving LDS accesses across the barrier.
+    // sched_barrier(0): nothing (MFMAs and folds included) is moved across
+    // the step boundary by the instruction scheduler
+    __builtin_amdgcn_sched_barrier(0);
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 
     // All LDS reads of this block first, then the DMA for block kb+2: no LDS
     // read follows a DMA issue inside a step, so the compiler never has to
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
     for (int j = 0; j < NJ; ++j) {
       bx[j] = pair(xt + x_lo + j * 2048, xt + x_hi + j * 2048);
       const float t = sxl[wm * WM + j * 16 + lrow];
-      c[j] = kLayout == kWgrad ? t : t * wsc;
+      c[j] = live ? (kLayout == kWgrad ? t : t * wsc) : 0.f;
     }
     v8i a[NI];
 #pragma unroll
@@ -297,30 +307,33 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
       for (int i = 0; i < NI; ++i) rs[i] = *reinterpret_cast<const float4*>(swl + wn * WN + i * 16 + lgrp * 4);
     }
     __asm__ volatile("" ::: "memory");
-    if (kb + 2 < KB) issue_loads(kb + 2, wnx, xnx);
+    // Block kb+2 streams into the stage freed by block kb-1.  The last two
+    // steps have no block kb+2; they reload block KB-1 into that free stage
+    // (in bounds, never read) so the DMA stays unconditional and keeps its
+    // place between the MFMAs.
+    const int kb_pf = kb + 2 < KB ? kb + 2 : KB - 1;
 
-    // Software pipeline: the MFMAs of subtile row i are issued before the FP32
-    // folds of row i-1, so the matrix core runs while the VALU folds.
-    auto fold = [&](int i, const v4f (&P)[NJ]) {
+    // Software pipeline over the 8 subtile rows: the MFMAs of row i, each
+    // followed by the FP32 fold of row i-1's partial sum in the same column
+    // (issued four MFMAs earlier, so already complete), with two of block
+    // kb+2's DMA instructions per row.  The matrix core, the VALU and the
+    // vector-memory unit then work side by side instead of in turns.
+    auto fold = [&](int i, int j, const v4f& P) {
       if constexpr (kLayout == kWgrad) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          acc[i][j][0] = __builtin_fmaf(P[j][0] * rs[i].x, c[j], acc[i][j][0]);
-          acc[i][j][1] = __builtin_fmaf(P[j][1] * rs[i].y, c[j], acc[i][j][1]);
-          acc[i][j][2] = __builtin_fmaf(P[j][2] * rs[i].z, c[j], acc[i][j][2]);
-          acc[i][j][3] = __builtin_fmaf(P[j][3] * rs[i].w, c[j], acc[i][j][3]);
-        }
+        acc[i][j][0] = __builtin_fmaf(P[0] * rs[i].x, c[j], acc[i][j][0]);
+        acc[i][j][1] = __builtin_fmaf(P[1] * rs[i].y, c[j], acc[i][j][1]);
+        acc[i][j][2] = __builtin_fmaf(P[2] * rs[i].z, c[j], acc[i][j][2]);
+        acc[i][j][3] = __builtin_fmaf(P[3] * rs[i].w, c[j], acc[i][j][3]);
       } else {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(P[j][v], c[j], acc[i][j][v]);
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(P[v], c[j], acc[i][j][v]);
       }
     };
     v4f P0[NJ], P1[NJ];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       v4f (&Pc)[NJ] = (i & 1) ? P1 : P0;
+      v4f (&Pp)[NJ] = (i & 1) ? P0 : P1;
       // operands in AGPRs (the MFMA reads them there), leaving the VGPRs to
       // the accumulators and the partial sums the VALU folds
       __asm__ volatile("" : "+a"(a[i]));
@@ -332,19 +345,45 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
       for (int j = 0; j < NJ; ++j) {
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
         Pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bx[j], zero, 0, 0, 0, 127, 0, 127);
+        if (i > 0) fold(i - 1, j, Pp[j]);
       }
-      if (i > 0) fold(i - 1, (i & 1) ? P0 : P1);
+      if (i < kOpsPerBlock / 2) {
+        issue_load(kb_pf, 2 * i, wnx, xnx);
+        issue_load(kb_pf, 2 * i + 1, wnx, xnx);
+      }
     }
-    fold(NI - 1, ((NI - 1) & 1) ? P1 : P0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fold(NI - 1, j, ((NI - 1) & 1) ? P1[j] : P0[j]);
+    // instruction order: per MFMA one fold (4 VALU, 8 for Wgrad), and a DMA
+    // after every second MFMA of the first rows
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i > 0) __builtin_amdgcn_sched_group_barrier(0x002, kLayout == kWgrad ? 8 : 4, 0);
+        if ((j & 1) && i < kOpsPerBlock / 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    }
   };
 
+  // Prologue: blocks 0 and 1 (block 0 again when K has a single block), then
+  // whole rounds of three steps with no conditions inside: K is padded to a
+  // multiple of three blocks, and a padding step folds with scale 0 (its
+  // partial sums come from a reload of the last block, so they are finite
+  // unless a NaN has already reached the accumulator).  Every step issues the
+  // same 14 DMA instructions, so one vmcnt threshold marks block kb landed,
+  // and the compiler's wait tracking sees that the stage being read is the
+  // one that has landed.
   issue_loads(0, lds_w0, lds_x0);
-  if (KB > 1) issue_loads(1, lds_w1, lds_x1);
+  issue_loads(KB > 1 ? 1 : 0, lds_w1, lds_x1);
   for (int kb = 0; kb < KB; kb += 3) {
     step(kb, lds_w0, lds_x0, lds_w2, lds_x2);
-    if (kb + 1 < KB) step(kb + 1, lds_w1, lds_x1, lds_w0, lds_x0);
-    if (kb + 2 < KB) step(kb + 2, lds_w2, lds_x2, lds_w1, lds_x1);
+    step(kb + 1, lds_w1, lds_x1, lds_w0, lds_x0);
+    step(kb + 2, lds_w2, lds_x2, lds_w1, lds_x1);
   }
+  // the last step's reload DMA must land before the workgroup's LDS is released
+  wait_vm_lgkm0<0>();
 
   // ---- epilogue: round and store ----
 #pragma unroll

@@ -14,6 +14,9 @@ seeded synthetic inputs already resident in HBM:
   weights    128x128 quantization of W 18432x7168
   policy     one caller-scale (history policy) quantization of a 128x7168 tile
              with amax and saturation count, plus the history update
+  copy       a plain 1 GiB device-to-device copy (torch's copy kernel): the
+             measured HBM rate beside the 8 TB/s spec, and the known-size
+             kernel that calibrates the HBM byte counters
 
 `value` is the metric's headline: TFLOP/s of the fprop row including its
 quantization (2*M*N*K / (t_quant + t_gemm)), from HIP events on the launch
@@ -96,15 +99,16 @@ class Timer:
         self.count.clear()
 
 
-def traffic_from_profiles(kernel_src):
-    """HBM bytes per launch from the committed PMC summary, if the kernel
-    source it was taken from is unchanged; else None."""
-    path = os.path.join(ROOT, "profiles", "fprop_gemm_traffic.json")
+def traffic_from_profiles(record, kernel_src):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) from a
+    committed PMC summary under profiles/, if the kernel source it was taken
+    from is unchanged; else None."""
+    path = os.path.join(ROOT, "profiles", record)
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        digest = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+        digest = hashlib.sha256(open(os.path.join(ROOT, kernel_src), "rb").read()).hexdigest()
         if rec.get("source_sha256") != digest:
             return None
         return rec.get("hbm_bytes_per_launch")
@@ -183,6 +187,9 @@ def main():
         d["hist"] = torch.ones((56, 128), dtype=torch.float32, device="cuda")
         d["sp"] = torch.ones((56, 128), dtype=torch.float32, device="cuda")
         d["sat"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if want("copy"):
+        d["cp_src"] = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        d["cp_dst"] = torch.empty_like(d["cp_src"])
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
 
@@ -220,21 +227,30 @@ def main():
                 fp8.quant_act_1x128(d["xp"], "row", scales_in=d["sp"], return_amax=True,
                                     sat_count=d["sat"])
             tm.region("policy", pol)
+        if want("copy"):
+            tm.region("copy", lambda: d["cp_dst"].copy_(d["cp_src"]))
 
     for _ in range(args.warmup):
         step()
         tm.collect()
     tm.reset()
     torch.cuda.synchronize()
+    # A short spin on the stream lets the host queue the timed steps ahead of
+    # the GPU, so each region's events bracket GPU work only (no host latency).
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(2_000_000)
     t_start = time.perf_counter()
+    ev_start = torch.cuda.Event(enable_timing=True)
+    ev_end = torch.cuda.Event(enable_timing=True)
+    ev_start.record()
     for i in range(args.steps):
         step()
-        if (i + 1) % 5 == 0:
-            tm.collect()
+    ev_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    steps_ms = ev_start.elapsed_time(ev_end)
     tm.collect()
-    log(f"timed {args.steps} steps in {wall:.2f} s")
+    log(f"timed {args.steps} steps: {steps_ms:.2f} ms on the GPU, {wall:.2f} s wall")
 
     rows = {}
     if want("quantizer"):
@@ -252,7 +268,7 @@ def main():
                          "TFLOP/s_incl_quant": value, "TFLOP/s_gemm": F3 / tg / 1e9,
                          "quant_GB/s": 4096 * 7168 * (3 + 4 / 128) / tq / 1e6}
         achieved = F3 / tg / 1e9
-        traffic = traffic_from_profiles(os.path.join(ROOT, "fine_grained_fp8_amd", "csrc", "gemm.hip"))
+        traffic = traffic_from_profiles("fprop_gemm_traffic.json", "fine_grained_fp8_amd/csrc/gemm.hip")
         roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": traffic,
                     "kernel": "block_gemm_kernel<FPROP,bf16> 4096x18432x7168",
@@ -276,6 +292,9 @@ def main():
         rows["weights"] = {"ms": t, "GB/s": B / t / 1e6}
     if want("policy"):
         rows["policy"] = {"ms": tm.mean_ms("policy")}
+    if want("copy"):
+        t = tm.mean_ms("copy")
+        rows["copy"] = {"ms": t, "GB/s": 2.0 * (1 << 30) / t / 1e6, "bytes": 2 * (1 << 30)}
 
     cpu = None
     if not args.no_cpu_baseline and want("fprop"):
@@ -291,7 +310,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": wall * 1e3 / args.steps,
+        "ms_per_step": steps_ms / args.steps,
+        "wall_s": wall,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -302,7 +322,9 @@ def main():
                    "M": 4096, "N": 18432, "K": 7168},
         "roofline": roofline,
         "roofline_quantizer": ({"bound": "hbm", "achieved": rows["quantizer"]["GB/s"], "peak": PEAK_HBM_GBPS,
-                                "unit": "GB/s", "frac": rows["quantizer"]["hbm_frac"], "traffic": None,
+                                "unit": "GB/s", "frac": rows["quantizer"]["hbm_frac"],
+                                "traffic": traffic_from_profiles("quant_rows_traffic.json",
+                                                                 "fine_grained_fp8_amd/csrc/quant.hip"),
                                 "kernel": "quant_rows_kernel<online> 8192x7168"}
                                if "quantizer" in rows else None),
         "cpu_baseline": cpu,

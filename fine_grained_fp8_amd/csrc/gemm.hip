@@ -4,7 +4,7 @@
 //
 // Sources: "FP8 Mixed Precision: DeepSeek-V3 Training Architecture" section 3
 // (E4M3 products, FP32 accumulators, block scale product applied to the
-// accumulated sums); "Fine-Grained Quantization in DeepSeek" section 4
+// accumulated sums); "Fine-Grained FP8 Quantization in DeepSeek" section 4
 // (FP8 values and local scales loaded by the kernel, products accumulated in
 // a wider type; scale application, transpose layout and epilogue decide the
 // speed); "Introduction to LLM Quantization" section 2 steps 3-4 (block

@@ -3,7 +3,7 @@
 // blocks (optionally also writing the transposed codes), the amax-history
 // update of the delayed-scaling policy, and the bare saturating E4M3 cast.
 //
-// Sources: "Fine-Grained Quantization in DeepSeek" sections 2-3 (1x128 tiles,
+// Sources: "Fine-Grained FP8 Quantization in DeepSeek" sections 2-3 (1x128 tiles,
 // 128x128 blocks, scale metadata produced efficiently and laid out for the
 // GEMM); "FP8 Mixed Precision: DeepSeek-V3 Training Architecture" section 1
 // (scale = block max / 448, clip to +-448); "Online Quantization During
@@ -15,18 +15,19 @@
 namespace fp8bs {
 
 // ---------------------------------------------------------------------------
-// 1x128 row tiles.  One wave owns 64 rows x one 128-column K block: 16 loads
-// of 4 tiles each (a tile is one 16-lane DPP row holding 8 BF16 per lane), so
-// the 64 scales of the block are written as one contiguous 256-byte store
-// into the MN-major scale array [K/128][ld_s].  A workgroup's four waves take
-// four consecutive K blocks of the same 64 rows.
+// 1x128 row tiles.  One wave owns 4*kG rows x one 128-column K block: kG
+// loads of 4 tiles each (a tile is one 16-lane DPP row holding 8 BF16 per
+// lane), so the block's 4*kG scales are written as one contiguous store into
+// the MN-major scale array [K/128][ld_s].  A workgroup's four waves take four
+// consecutive K blocks of the same rows.
 // ---------------------------------------------------------------------------
-template <bool kExternal>
+template <bool kExternal, int kG>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t kblocks,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int64_t ld_s,
     const float* __restrict__ scales_in, float* __restrict__ amax_out,
     uint32_t* __restrict__ sat_count) {
+  constexpr int kRows = 4 * kG;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t nkbg = (kblocks + 3) >> 2;
@@ -35,12 +36,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   if (kb >= kblocks) return;                 // whole wave idle; no block barriers below
   const int sub = lane >> 4;
   const int l16 = lane & 15;
-  const int64_t r0 = rb * 64;
+  const int64_t r0 = rb * kRows;
   const uint16_t* xb = x + kb * 128 + l16 * 8;
 
-  uint4 v[16];
+  uint4 v[kG];
 #pragma unroll
-  for (int g = 0; g < 16; ++g) {
+  for (int g = 0; g < kG; ++g) {
     const int64_t row = r0 + 4 * g + sub;
     v[g] = row < rows ? *reinterpret_cast<const uint4*>(xb + row * ldx) : make_uint4(0, 0, 0, 0);
   }
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   float my_s = 0.0f, my_amax = 0.0f;
   uint32_t sat = 0;
 #pragma unroll
-  for (int g = 0; g < 16; ++g) {
+  for (int g = 0; g < kG; ++g) {
     const int64_t row = r0 + 4 * g + sub;
     const uint32_t t = row16_max_u32(absmax_bits8(v[g]));
     float s;
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     if ((lane >> 2) == g) { my_s = sg; my_amax = ag; }
   }
   const int64_t row = r0 + lane;
-  if (row < rows) {
+  if (lane < kRows && row < rows) {
     if (!kExternal) scales[kb * ld_s + row] = my_s;
     if (amax_out) amax_out[kb * ld_s + row] = my_amax;
   }
@@ -292,13 +293,17 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
                              uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
                              const float* scales_in, float* amax_out, uint32_t* sat_count,
                              hipStream_t stream) {
+  // 16 rows per wave: measured on 8192x7168 with the input streamed from HBM,
+  // 16 rows run ~15% faster than 64 (more, shorter waves keep reads and
+  // writes overlapped and leave a shorter tail)
+  constexpr int kG = 4;
   const int64_t kblocks = cols / 128;
-  const int64_t nblocks = ((rows + 63) / 64) * ((kblocks + 3) / 4);
+  const int64_t nblocks = ((rows + 4 * kG - 1) / (4 * kG)) * ((kblocks + 3) / 4);
   if (scales_in) {
-    hipLaunchKernelGGL(quant_rows_kernel<true>, dim3((unsigned)nblocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((quant_rows_kernel<true, kG>), dim3((unsigned)nblocks), dim3(256), 0, stream,
                        x, rows, ldx, kblocks, q, ldq, scales, ld_s, scales_in, amax_out, sat_count);
   } else {
-    hipLaunchKernelGGL(quant_rows_kernel<false>, dim3((unsigned)nblocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((quant_rows_kernel<false, kG>), dim3((unsigned)nblocks), dim3(256), 0, stream,
                        x, rows, ldx, kblocks, q, ldq, scales, ld_s, scales_in, amax_out, sat_count);
   }
   return hipGetLastError();

@@ -5,19 +5,21 @@
  * What the library computes (sources are the pages' titles and sections):
  *
  *  - Online activation quantization with one FP32 scale per 1x128 tile of
- *    contiguous channels of one token ("Fine-Grained Quantization in
+ *    contiguous channels of one token ("Fine-Grained FP8 Quantization in
  *    DeepSeek", section 2; "FP8 Mixed Precision: DeepSeek-V3 Training
  *    Architecture", section 1 item 1; "Introduction to LLM Quantization",
  *    section 5).
  *  - Weight quantization with one FP32 scale per 128x128 block ("Fine-Grained
- *    Quantization in DeepSeek", section 3; "FP8 Mixed Precision", section 1
- *    item 2 and its block-scale equations).
+ *    FP8 Quantization in DeepSeek", section 3; "FP8 Mixed Precision:
+ *    DeepSeek-V3 Training Architecture", section 1 item 2 and its block-scale
+ *    equations).
  *  - Block-scaled FP8 GEMM: E4M3 products accumulated in FP32, each 128-wide
  *    K block's partial sum multiplied by its two scales, blocks summed in
- *    FP32, result rounded once to BF16 (or kept FP32) ("FP8 Mixed Precision",
- *    section 3 "Decoupled Accumulation in Tensor Core GEMMs"; "Fine-Grained
- *    Quantization in DeepSeek", section 4; "Introduction to LLM
- *    Quantization", section 2 steps 1-4), in the forward (Fprop),
+ *    FP32, result rounded once to BF16 (or kept FP32) ("FP8 Mixed Precision:
+ *    DeepSeek-V3 Training Architecture", section 3 "Decoupled Accumulation in
+ *    Tensor Core GEMMs"; "Fine-Grained FP8 Quantization in DeepSeek", section
+ *    4; "Introduction to LLM Quantization", section 2 steps 1-4), in the
+ *    forward (Fprop),
  *    input-gradient (Dgrad) and weight-gradient (Wgrad) layouts
  *    ("Introduction to LLM Quantization", section 1 items 2-3).
  *

@@ -1,6 +1,6 @@
 """The pages' worked examples, computed with the oracle (test infrastructure only).
 
-* ``two_tiles`` - "Fine-Grained Quantization in DeepSeek", worked example:
+* ``two_tiles`` - "Fine-Grained FP8 Quantization in DeepSeek", worked example:
   one 128-value tile centred near 0.1 and one containing a 20.0 outlier;
   reconstruction error under one global scale versus one scale per tile, and
   scale bytes per activation value.

@@ -6,7 +6,7 @@ Sources:
   ("Decoupled Accumulation in Tensor Core GEMMs"): E4M3 x E4M3 products,
   partial sums held in FP32, and the block scale product s_A * s_B multiplied
   into the accumulated sum rather than into the operands.
-* "Fine-Grained Quantization in DeepSeek", section 4: kernels load FP8 values
+* "Fine-Grained FP8 Quantization in DeepSeek", section 4: kernels load FP8 values
   and their local scales, multiply in hardware and accumulate in a wider
   type.
 * "Introduction to LLM Quantization", section 2 (fine-grained steps 1-4: one

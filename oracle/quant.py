@@ -2,7 +2,7 @@
 
 Sources:
 
-* "Fine-Grained Quantization in DeepSeek", sections 2 (activations: one scale
+* "Fine-Grained FP8 Quantization in DeepSeek", sections 2 (activations: one scale
   per tile of 128 contiguous values) and 3 (weights: one scale per 128x128
   block).
 * "FP8 Mixed Precision: DeepSeek-V3 Training Architecture", section 1: the

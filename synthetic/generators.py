@@ -2,7 +2,7 @@
 
 Distributions follow the workloads the pages describe for fine-grained FP8:
 Gaussian activations whose outliers concentrate in a few fixed channels
-("Fine-Grained Quantization in DeepSeek", failure-modes list: Gaussian-only
+("Fine-Grained FP8 Quantization in DeepSeek", failure-modes list: Gaussian-only
 tests under-represent outliers), Gaussian weights, small Gaussian gradients,
 a tile whose spread doubles over 100 steps with one rare 20-sigma spike
 ("Online Quantization During Training", worked example), and per-expert

@@ -109,6 +109,73 @@ __device__ __forceinline__ v8i read_operand_t(const uint8_t* tile, int n_sub, in
   return out;
 }
 
+// Tile of workgroup `blockIdx.x`: token rows [m0, min(m0 + BM, m_end)) and
+// output columns [n0, n0 + BN); Bp / sBp point at the tile's group in the
+// grouped case.  Returns false for the padding workgroups of a grouped launch.
+__device__ __forceinline__ bool decode_tile(const GemmProblem& p, int64_t total_tiles, bool grouped,
+                                            int64_t& m0, int64_t& m_end, int64_t& n0,
+                                            const uint8_t*& Bp, const float*& sBp) {
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+  Bp = p.B;
+  sBp = p.sB;
+  if (grouped) {
+    if (b >= total_tiles) return false;
+    int64_t cum = 0, lo = 0, hi = 0, ntm = 0;
+    int g = 0;
+    for (; g < p.groups; ++g) {
+      lo = p.offsets[g];
+      hi = p.offsets[g + 1];
+      ntm = (hi - lo + BM - 1) / BM;
+      if (b < cum + ntm * tiles_n) break;
+      cum += ntm * tiles_n;
+    }
+    if (g >= p.groups) return false;
+    const int64_t local = b - cum;
+    m0 = lo + (local / tiles_n) * BM;
+    n0 = (local % tiles_n) * BN;
+    m_end = hi;
+    Bp += (int64_t)g * p.N * p.ldb;
+    sBp += (int64_t)g * (p.N / 128) * (p.K / BK);
+  } else {
+    const int64_t tiles_m = (p.M + BM - 1) / BM;
+    int64_t tm, tn;
+    grouped_order(b, tiles_m, tiles_n, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+    m_end = p.M;
+  }
+  return true;
+}
+
+// Round and store 4 consecutive outputs (n..n+3) of row m; columns past N
+// are dropped.
+template <bool kOutF32>
+__device__ __forceinline__ void store4(const GemmProblem& p, int64_t m, int64_t n, const v4f& r) {
+  if constexpr (kOutF32) {
+    float* dst = reinterpret_cast<float*>(p.C) + m * p.ldc + n;
+    if (n + 3 < p.N) {
+      *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1], r[2], r[3]);
+    } else {
+      for (int v = 0; v < 4 && n + v < p.N; ++v) dst[v] = r[v];
+    }
+  } else {
+    __bf16 h0 = (__bf16)r[0], h1 = (__bf16)r[1], h2 = (__bf16)r[2], h3 = (__bf16)r[3];
+    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+    uint16_t* dst = reinterpret_cast<uint16_t*>(p.C) + m * p.ldc + n;
+    if (n + 3 < p.N) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+    } else {
+      const uint16_t hv[4] = {(uint16_t)(w0 & 0xFFFF), (uint16_t)(w0 >> 16),
+                              (uint16_t)(w1 & 0xFFFF), (uint16_t)(w1 >> 16)};
+      for (int v = 0; v < 4 && n + v < p.N; ++v) dst[v] = hv[v];
+    }
+  }
+}
+
 // s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
 // operations of this wave are outstanding and all LDS/scalar ones are done.
 template <int vm>
@@ -132,39 +199,12 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
-  const int64_t tiles_n = (p.N + BN - 1) / BN;
 
   // ---- tile coordinates ----
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
   int64_t m0, m_end, n0;
-  const uint8_t* Bp = p.B;
-  const float* sBp = p.sB;
-  if constexpr (kGrouped) {
-    if (b >= total_tiles) return;
-    int64_t cum = 0, lo = 0, hi = 0, ntm = 0;
-    int g = 0;
-    for (; g < p.groups; ++g) {
-      lo = p.offsets[g];
-      hi = p.offsets[g + 1];
-      ntm = (hi - lo + BM - 1) / BM;
-      if (b < cum + ntm * tiles_n) break;
-      cum += ntm * tiles_n;
-    }
-    if (g >= p.groups) return;
-    const int64_t local = b - cum;
-    m0 = lo + (local / tiles_n) * BM;
-    n0 = (local % tiles_n) * BN;
-    m_end = hi;
-    Bp += (int64_t)g * p.N * p.ldb;
-    sBp += (int64_t)g * (p.N / 128) * (p.K / BK);
-  } else {
-    const int64_t tiles_m = (p.M + BM - 1) / BM;
-    int64_t tm, tn;
-    grouped_order(b, tiles_m, tiles_n, tm, tn);
-    m0 = tm * BM;
-    n0 = tn * BN;
-    m_end = p.M;
-  }
+  const uint8_t* Bp;
+  const float* sBp;
+  if (!decode_tile(p, total_tiles, kGrouped, m0, m_end, n0, Bp, sBp)) return;
   const int KB = (int)(p.K / BK);
   const int rows_m = (int)(m_end - m0 < BM ? m_end - m0 : BM);   // valid token rows in the tile
   const int rows_n = (int)(p.N - n0 < BN ? p.N - n0 : BN);       // valid output columns
@@ -394,41 +434,253 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
     for (int i = 0; i < NI; ++i) {
       const int64_t n = n0 + wn * WN + i * 16 + lgrp * 4;
       if (n >= p.N) continue;
-      const v4f r = acc[i][j];
-      if constexpr (kOutF32) {
-        float* dst = reinterpret_cast<float*>(p.C) + m * p.ldc + n;
-        if (n + 3 < p.N) {
-          *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1], r[2], r[3]);
-        } else {
-          for (int v = 0; v < 4 && n + v < p.N; ++v) dst[v] = r[v];
-        }
+      store4<kOutF32>(p, m, n, acc[i][j]);
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Direct-weight kernel (Fprop, Wgrad, grouped Fprop).
+//
+// Each wave owns 64 output columns (n) x all 128 token rows (m) of the
+// 256 x 128 workgroup tile.  Its weight-side rows are private, so they skip
+// LDS: they are loaded from memory straight into registers in MFMA operand
+// layout, four K blocks deep.  Only the token-side tile, shared by the four
+// waves, goes through LDS (four stages, DMA).  Per K step and CU this moves
+// 80 KB through LDS (16 KB DMA writes + 64 KB operand reads) and 49 KB through
+// the vector-memory unit, both below the 32 MFMAs per wave of the step.
+//
+// k order inside an operand register: lane group g (= lane / 16) holds bytes
+// 16g..16g+15 and 64+16g..64+16g+15 of the 128-byte K block (two aligned
+// 64-byte halves per load instruction).  Both operands use the same order, so
+// the MFMA contracts the same 128 products; each aligned run of 8 k stays
+// together inside the MFMA.
+// ---------------------------------------------------------------------------
+constexpr int kDS = 4;                         // LDS stages = weight register buffers
+constexpr int DNI = 4, DNJ = 8;                // wave tile: 64 (n) x 128 (m)
+constexpr int kDScaleOff = BM * BK;            // token-side scales (1 KB DMA footprint)
+constexpr int kDWScaleOff = kDScaleOff + 1024; // weight-side scales (1 KB)
+constexpr int kDStage = kDWScaleOff + 1024;    // 18 KB per stage
+constexpr int kDOpsPerBlock = 4 + 1 + 1 + 8;   // DMA: 4 token rows, 2 scale vectors; 8 weight loads
+
+template <int kLayout, bool kOutF32, bool kGrouped>
+__global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProblem p, int64_t total_tiles) {
+  static_assert(kLayout != kDgrad, "Dgrad reads the weights transposed through LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s0[kDStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s1[kDStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s2[kDStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s3[kDStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 15, lgrp = lane >> 4;
+
+  int64_t m0, m_end, n0;
+  const uint8_t* Bp;
+  const float* sBp;
+  if (!decode_tile(p, total_tiles, kGrouped, m0, m_end, n0, Bp, sBp)) return;
+  const int KB = (int)(p.K / BK);
+  const int rows_m = (int)(m_end - m0 < BM ? m_end - m0 : BM);
+  const int rows_n = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+
+  // token-side tile: rows m0.., DMA'd 8 rows x 128 B per instruction, 16-byte
+  // chunks XOR-swizzled by row & 7 (row & 7 == (lane >> 3) & 7 here)
+  const __amdgpu_buffer_rsrc_t rsrc_x = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.A + m0 * p.lda), (short)0, rows_m * (int)p.lda, (int)kRsrcWord3);
+  const int xrow = wave * 32 + (lane >> 3);
+  const uint32_t off_x = (uint32_t)(xrow * (int)p.lda + (((lane & 7) ^ (lane >> 3)) << 4));
+  // weight-side rows n0 + 64 wave + 16 i + lrow, loaded straight into registers
+  const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Bp + n0 * p.ldb), (short)0, rows_n * (int)p.ldb, (int)kRsrcWord3);
+  const uint32_t off_w = (uint32_t)((wave * 64 + lrow) * (int)p.ldb + lgrp * 16);
+  const uint32_t w_istride = (uint32_t)(16 * p.ldb);
+  // weight-side scales: Fprop - the wave's 128x128 weight block (every lane
+  // fetches the same float); Wgrad - the workgroup's 256 per-column scales
+  const int64_t sw_elems = kLayout == kFprop ? (p.N / 128) * p.ld_sb : 0;
+  const __amdgpu_buffer_rsrc_t rsrc_sw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)sBp, (short)0, kLayout == kFprop ? (int)(sw_elems * 4) : 0, (int)kRsrcWord3);
+  const uint32_t sw_off = (uint32_t)(((n0 + 64 * wave) / 128) * p.ld_sb) * 4u;
+
+  auto issue_load = [&](int kb, int op, uint8_t* st, v8i (&wr)[DNI]) {
+    if (op < 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_x, (lds_ptr_t)(st + (wave * 4 + op) * 1024), 16,
+                                               off_x + (uint32_t)(kb * BK + op * 8 * (int)p.lda), 0, 0, 0);
+    } else if (op == 4) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.sA + (int64_t)kb * p.ld_sa + m0), (short)0, rows_m * 4, (int)kRsrcWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + kDScaleOff), 16, (uint32_t)(lane * 16), 0, 0, 0);
+    } else if (op == 5) {
+      if constexpr (kLayout == kWgrad) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(sBp + (int64_t)kb * p.ld_sb + n0), (short)0, rows_n * 4, (int)kRsrcWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + kDWScaleOff), 16, (uint32_t)(lane * 16), 0, 0, 0);
       } else {
-        __bf16 h0 = (__bf16)r[0], h1 = (__bf16)r[1], h2 = (__bf16)r[2], h3 = (__bf16)r[3];
-        const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-        uint16_t* dst = reinterpret_cast<uint16_t*>(p.C) + m * p.ldc + n;
-        if (n + 3 < p.N) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-        } else {
-          const uint16_t hv[4] = {(uint16_t)(w0 & 0xFFFF), (uint16_t)(w0 >> 16),
-                                  (uint16_t)(w1 & 0xFFFF), (uint16_t)(w1 >> 16)};
-          for (int v = 0; v < 4 && n + v < p.N; ++v) dst[v] = hv[v];
-        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_sw, (lds_ptr_t)(st + kDWScaleOff + wave * 256), 4,
+                                                 sw_off + (uint32_t)kb * 4u, 0, 0, 0);
       }
+    } else {
+      const int i = (op - 6) >> 1, h = (op - 6) & 1;
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc_w, off_w + (uint32_t)i * w_istride + (uint32_t)(h * 64 + kb * BK), 0, 0);
+      wr[i][4 * h + 0] = v[0];
+      wr[i][4 * h + 1] = v[1];
+      wr[i][4 * h + 2] = v[2];
+      wr[i][4 * h + 3] = v[3];
+    }
+  };
+
+  // swizzled LDS addresses of this lane's token-side operand halves: row
+  // 16 j + lrow (row & 7 == lrow & 7), bytes 16 lgrp.. and 64 + 16 lgrp..
+  const int sw = lrow & 7;
+  const int x_lo = lrow * 128 + ((lgrp ^ sw) << 4);
+  const int x_hi = lrow * 128 + (((4 + lgrp) ^ sw) << 4);
+
+  v4f acc[DNI][DNJ];
+#pragma unroll
+  for (int i = 0; i < DNI; ++i)
+#pragma unroll
+    for (int j = 0; j < DNJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8i w0[DNI], w1[DNI], w2[DNI], w3[DNI];
+
+  // ---- one K block: token tile in stage st, weights in wc; block kb+3
+  // streams into stage sf (read in step kb-1) and registers wf ----
+  auto step = [&](int kb, const uint8_t* st, v8i (&wc)[DNI], uint8_t* sf, v8i (&wf)[DNI]) {
+    wait_vm_lgkm0<2 * kDOpsPerBlock>();   // block kb landed; kb+1 and kb+2 may fly
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const bool live = kb < KB;
+    const int kb_pf = kb + 3 < KB ? kb + 3 : KB - 1;
+
+    const float* sxl = reinterpret_cast<const float*>(st + kDScaleOff);
+    const float* swl = reinterpret_cast<const float*>(st + kDWScaleOff);
+    float wsc = 1.f;
+    if constexpr (kLayout == kFprop) wsc = swl[wave * 64];
+    // scales first: their LDS reads complete ahead of the operand reads, so
+    // the waits for them do not wait for the operands
+    float c[DNJ];
+#pragma unroll
+    for (int j = 0; j < DNJ; ++j) {
+      const float t = sxl[j * 16 + lrow];
+      c[j] = live ? (kLayout == kWgrad ? t : t * wsc) : 0.f;
+    }
+    float4 rs[DNI];
+    if constexpr (kLayout == kWgrad) {
+#pragma unroll
+      for (int i = 0; i < DNI; ++i)
+        rs[i] = *reinterpret_cast<const float4*>(swl + wave * 64 + i * 16 + lgrp * 4);
+    }
+    __asm__ volatile("" ::: "memory");
+    v8i bx[DNJ];
+#pragma unroll
+    for (int j = 0; j < DNJ; ++j) bx[j] = pair(st + x_lo + j * 2048, st + x_hi + j * 2048);
+    __asm__ volatile("" ::: "memory");
+
+    auto fold = [&](int j, int i, const v4f& P) {
+      if constexpr (kLayout == kWgrad) {
+        acc[i][j][0] = __builtin_fmaf(P[0] * rs[i].x, c[j], acc[i][j][0]);
+        acc[i][j][1] = __builtin_fmaf(P[1] * rs[i].y, c[j], acc[i][j][1]);
+        acc[i][j][2] = __builtin_fmaf(P[2] * rs[i].z, c[j], acc[i][j][2]);
+        acc[i][j][3] = __builtin_fmaf(P[3] * rs[i].w, c[j], acc[i][j][3]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(P[v], c[j], acc[i][j][v]);
+      }
+    };
+    // rows j of 4 MFMAs (the wave's 4 weight subtiles against token subtile
+    // j), each MFMA followed by the fold of the same subtile's partial from
+    // row j-1 (issued four MFMAs earlier); two of block kb+3's loads per row
+    v4f P0[DNI], P1[DNI];
+    // operands in AGPRs (the MFMA reads them there), leaving the VGPRs to the
+    // accumulators, the partial sums and the scales
+#pragma unroll
+    for (int i = 0; i < DNI; ++i) __asm__ volatile("" : "+a"(wc[i]));
+#pragma unroll
+    for (int j = 0; j < DNJ; ++j) {
+      v4f (&Pc)[DNI] = (j & 1) ? P1 : P0;
+      v4f (&Pp)[DNI] = (j & 1) ? P0 : P1;
+      __asm__ volatile("" : "+a"(bx[j]));
+#pragma unroll
+      for (int i = 0; i < DNI; ++i) {
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+        Pc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wc[i], bx[j], zero, 0, 0, 0, 127, 0, 127);
+        if (j > 0) fold(j - 1, i, Pp[i]);
+      }
+      if (j < kDOpsPerBlock / 2) {
+        issue_load(kb_pf, 2 * j, sf, wf);
+        issue_load(kb_pf, 2 * j + 1, sf, wf);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < DNI; ++i) fold(DNJ - 1, i, ((DNJ - 1) & 1) ? P1[i] : P0[i]);
+#pragma unroll
+    for (int j = 0; j < DNJ; ++j) {
+#pragma unroll
+      for (int i = 0; i < DNI; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (j > 0) __builtin_amdgcn_sched_group_barrier(0x002, kLayout == kWgrad ? 8 : 4, 0);
+        if ((i & 1) && j < kDOpsPerBlock / 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    }
+  };
+
+  // Prologue: blocks 0-2 (repeating the last block when K is shorter), then
+  // whole rounds of four steps with no conditions inside: K is padded to a
+  // multiple of four blocks and a padding step folds with scale 0.
+  {
+    const int b1 = KB > 1 ? 1 : KB - 1, b2 = KB > 2 ? 2 : KB - 1;
+#pragma unroll
+    for (int op = 0; op < kDOpsPerBlock; ++op) issue_load(0, op, lds_s0, w0);
+#pragma unroll
+    for (int op = 0; op < kDOpsPerBlock; ++op) issue_load(b1, op, lds_s1, w1);
+#pragma unroll
+    for (int op = 0; op < kDOpsPerBlock; ++op) issue_load(b2, op, lds_s2, w2);
+  }
+  for (int kb = 0; kb < KB; kb += 4) {
+    step(kb, lds_s0, w0, lds_s3, w3);
+    step(kb + 1, lds_s1, w1, lds_s0, w0);
+    step(kb + 2, lds_s2, w2, lds_s1, w1);
+    step(kb + 3, lds_s3, w3, lds_s2, w2);
+  }
+  // the last steps' reload DMA must land before the workgroup's LDS is released
+  wait_vm_lgkm0<0>();
+
+  // ---- epilogue: lane holds 4 consecutive n of row m for every (i, j) ----
+#pragma unroll
+  for (int j = 0; j < DNJ; ++j) {
+    const int64_t m = m0 + j * 16 + lrow;
+    if (m >= m_end) continue;
+#pragma unroll
+    for (int i = 0; i < DNI; ++i) {
+      const int64_t n = n0 + wave * 64 + i * 16 + lgrp * 4;
+      if (n >= p.N) continue;
+      store4<kOutF32>(p, m, n, acc[i][j]);
     }
   }
 }
 
 template <int kLayout, bool kGrouped>
 hipError_t launch_typed(const GemmProblem& p, hipStream_t stream, int64_t grid, int64_t total) {
-  if (p.out_fp32) {
-    hipLaunchKernelGGL((block_gemm_kernel<kLayout, true, kGrouped>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, p, total);
+  if constexpr (kLayout == kDgrad) {
+    if (p.out_fp32) {
+      hipLaunchKernelGGL((block_gemm_kernel<kLayout, true, kGrouped>), dim3((unsigned)grid),
+                         dim3(kThreads), 0, stream, p, total);
+    } else {
+      hipLaunchKernelGGL((block_gemm_kernel<kLayout, false, kGrouped>), dim3((unsigned)grid),
+                         dim3(kThreads), 0, stream, p, total);
+    }
   } else {
-    hipLaunchKernelGGL((block_gemm_kernel<kLayout, false, kGrouped>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, p, total);
+    if (p.out_fp32) {
+      hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped>), dim3((unsigned)grid),
+                         dim3(kThreads), 0, stream, p, total);
+    } else {
+      hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped>), dim3((unsigned)grid),
+                         dim3(kThreads), 0, stream, p, total);
+    }
   }
   return hipGetLastError();
 }

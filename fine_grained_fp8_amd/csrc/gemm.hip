@@ -462,7 +462,9 @@ constexpr int DNI = 4, DNJ = 8;                // wave tile: 64 (n) x 128 (m)
 constexpr int kDScaleOff = BM * BK;            // token-side scales (1 KB DMA footprint)
 constexpr int kDWScaleOff = kDScaleOff + 1024; // weight-side scales (1 KB)
 constexpr int kDStage = kDWScaleOff + 1024;    // 18 KB per stage
-constexpr int kDOpsPerBlock = 4 + 1 + 1 + 8;   // DMA: 4 token rows, 2 scale vectors; 8 weight loads
+constexpr int kDDmaOps = 4 + 1 + 1;            // DMA per block: 4 token-row, 2 scale instructions
+constexpr int kDWOps = 8;                      // weight loads per block
+constexpr int kDOpsPerBlock = kDDmaOps + kDWOps;
 
 template <int kLayout, bool kOutF32, bool kGrouped>
 __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProblem p, int64_t total_tiles) {
@@ -546,15 +548,23 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
 
   // ---- one K block: token tile in stage st, weights in wc; block kb+3
   // streams into stage sf (read in step kb-1) and registers wf ----
-  auto step = [&](int kb, const uint8_t* st, v8i (&wc)[DNI], uint8_t* sf, v8i (&wf)[DNI]) {
-    wait_vm_lgkm0<2 * kDOpsPerBlock>();   // block kb landed; kb+1 and kb+2 may fly
+  // Issue order: the token tile and scales of block kb+2 (DMA), then the
+  // weights of block kb+3, in every step.  At the start of step kb the ops
+  // issued after block kb's DMA are block kb+1's weights and all of step
+  // kb-1, so vmcnt(kDOpsPerBlock + kDWOps) marks block kb's tile and weights
+  // landed.  (The compiler does not count the LDS-DMA instructions in its own
+  // waits for the weight registers; with this order its stricter waits only
+  // cover data that is needed by then anyway.)
+  auto step = [&](int kb, const uint8_t* st, v8i (&wc)[DNI], uint8_t* sd, v8i (&wf)[DNI]) {
+    wait_vm_lgkm0<kDOpsPerBlock + kDWOps>();
     __builtin_amdgcn_sched_barrier(0);
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     const bool live = kb < KB;
-    const int kb_pf = kb + 3 < KB ? kb + 3 : KB - 1;
+    const int kb_d = kb + 2 < KB ? kb + 2 : KB - 1;   // token tile streamed this step
+    const int kb_w = kb + 3 < KB ? kb + 3 : KB - 1;   // weights streamed this step
 
     const float* sxl = reinterpret_cast<const float*>(st + kDScaleOff);
     const float* swl = reinterpret_cast<const float*>(st + kDWScaleOff);
@@ -575,10 +585,11 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
         rs[i] = *reinterpret_cast<const float4*>(swl + wave * 64 + i * 16 + lgrp * 4);
     }
     __asm__ volatile("" ::: "memory");
+    // token-side operands two rows ahead of their MFMAs: a burst of all 16
+    // reads would fill the LDS queue and stall the wave at issue
     v8i bx[DNJ];
-#pragma unroll
-    for (int j = 0; j < DNJ; ++j) bx[j] = pair(st + x_lo + j * 2048, st + x_hi + j * 2048);
-    __asm__ volatile("" ::: "memory");
+    bx[0] = pair(st + x_lo, st + x_hi);
+    bx[1] = pair(st + x_lo + 2048, st + x_hi + 2048);
 
     auto fold = [&](int j, int i, const v4f& P) {
       if constexpr (kLayout == kWgrad) {
@@ -603,16 +614,20 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     for (int j = 0; j < DNJ; ++j) {
       v4f (&Pc)[DNI] = (j & 1) ? P1 : P0;
       v4f (&Pp)[DNI] = (j & 1) ? P0 : P1;
+      if (j + 2 < DNJ) bx[j + 2] = pair(st + x_lo + (j + 2) * 2048, st + x_hi + (j + 2) * 2048);
       __asm__ volatile("" : "+a"(bx[j]));
 #pragma unroll
       for (int i = 0; i < DNI; ++i) {
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
         Pc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wc[i], bx[j], zero, 0, 0, 0, 127, 0, 127);
         if (j > 0) fold(j - 1, i, Pp[i]);
+        // instruction order = source order: one MFMA, then the fold of the
+        // partial it produced four MFMAs (20 instructions) earlier
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (j < kDOpsPerBlock / 2) {
-        issue_load(kb_pf, 2 * j, sf, wf);
-        issue_load(kb_pf, 2 * j + 1, sf, wf);
+        issue_load(2 * j < kDDmaOps ? kb_d : kb_w, 2 * j, sd, wf);
+        issue_load(2 * j + 1 < kDDmaOps ? kb_d : kb_w, 2 * j + 1, sd, wf);
       }
     }
 #pragma unroll
@@ -623,28 +638,35 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
       for (int i = 0; i < DNI; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (j > 0) __builtin_amdgcn_sched_group_barrier(0x002, kLayout == kWgrad ? 8 : 4, 0);
+        if (i == 0 && j + 2 < DNJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         if ((i & 1) && j < kDOpsPerBlock / 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     }
   };
 
-  // Prologue: blocks 0-2 (repeating the last block when K is shorter), then
-  // whole rounds of four steps with no conditions inside: K is padded to a
-  // multiple of four blocks and a padding step folds with scale 0.
+  // Prologue, in the steady-state order (weights of block 0; tile of block 0
+  // and weights of block 1; tile of block 1 and weights of block 2), blocks
+  // past K repeating the last block.  Then whole rounds of four steps with no
+  // conditions inside: K is padded to a multiple of four blocks and a padding
+  // step folds with scale 0.
   {
-    const int b1 = KB > 1 ? 1 : KB - 1, b2 = KB > 2 ? 2 : KB - 1;
+    auto clamp = [&](int b) { return b < KB ? b : KB - 1; };
 #pragma unroll
-    for (int op = 0; op < kDOpsPerBlock; ++op) issue_load(0, op, lds_s0, w0);
+    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(0, op, lds_s0, w0);
 #pragma unroll
-    for (int op = 0; op < kDOpsPerBlock; ++op) issue_load(b1, op, lds_s1, w1);
+    for (int op = 0; op < kDDmaOps; ++op) issue_load(0, op, lds_s0, w0);
 #pragma unroll
-    for (int op = 0; op < kDOpsPerBlock; ++op) issue_load(b2, op, lds_s2, w2);
+    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(1), op, lds_s1, w1);
+#pragma unroll
+    for (int op = 0; op < kDDmaOps; ++op) issue_load(clamp(1), op, lds_s1, w1);
+#pragma unroll
+    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(2), op, lds_s2, w2);
   }
   for (int kb = 0; kb < KB; kb += 4) {
-    step(kb, lds_s0, w0, lds_s3, w3);
-    step(kb + 1, lds_s1, w1, lds_s0, w0);
-    step(kb + 2, lds_s2, w2, lds_s1, w1);
-    step(kb + 3, lds_s3, w3, lds_s2, w2);
+    step(kb, lds_s0, w0, lds_s2, w3);
+    step(kb + 1, lds_s1, w1, lds_s3, w0);
+    step(kb + 2, lds_s2, w2, lds_s0, w1);
+    step(kb + 3, lds_s3, w3, lds_s1, w2);
   }
   // the last steps' reload DMA must land before the workgroup's LDS is released
   wait_vm_lgkm0<0>();

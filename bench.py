@@ -6,12 +6,13 @@ seeded synthetic inputs already resident in HBM:
   quantizer  1x128 online quantization of X 8192x7168 (outliers in 16 channels)
   fprop      1x128 quantization of X 4096x7168 + block-scaled GEMM
              Y = X W^T 4096x18432x7168 (W pre-quantized 128x128), BF16 out
-  backward   dY 4096x18432: 1x128 quantization + Dgrad dX = dY W (W read
-             transposed); 128x1 quantization of dY and X + Wgrad dW = dY^T X
-             (FP32 out)
+  backward   dY 4096x18432: 1x128 quantization + Dgrad dX = dY W from the
+             transposed weight codes W_q^T; 128x1 quantization of dY and X +
+             Wgrad dW = dY^T X (FP32 out).  Also reported: Dgrad reading W_q
+             as stored (transposed in LDS), "dgrad_lds".
   grouped    1x128 quantization of X 16384x7168 + one grouped launch over 8
              experts (multinomial token counts), W_e 2048x7168
-  weights    128x128 quantization of W 18432x7168
+  weights    128x128 quantization of W 18432x7168 with the transposed copy
   policy     one caller-scale (history policy) quantization of a 128x7168 tile
              with amax and saturation count, plus the history update
   copy       a plain 1 GiB device-to-device copy (torch's copy kernel): the
@@ -167,7 +168,7 @@ def main():
     if want("fprop") or want("backward"):
         host["x3"] = syn.activation_with_outliers(4096, 7168, seed=0)
         d["x3"] = to_dev(host["x3"], torch)
-        d["wq3"], d["ws3"], _ = fp8.quant_weight_128x128(d["w3"])         # pre-quantized, untimed
+        d["wq3"], d["ws3"], d["wq3t"] = fp8.quant_weight_128x128(d["w3"], transposed=True)  # untimed
     if want("backward"):
         d["dy4"] = to_dev(syn.gaussian((4096, 18432), seed=4, std=1e-3), torch)
     if want("grouped"):
@@ -207,7 +208,8 @@ def main():
         if want("backward"):
             ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
             dq, ds, _ = tm.region("dgrad.quant", lambda: fp8.quant_act_1x128(d["dy4"], "row"))
-            tm.region("dgrad.gemm", lambda: fp8.block_gemm("dgrad", dq, ds, d["wq3"], d["ws3"]))
+            tm.region("dgrad.gemm", lambda: fp8.block_gemm("dgrad_t", dq, ds, d["wq3t"], d["ws3"]))
+            tm.region("dgrad_lds.gemm", lambda: fp8.block_gemm("dgrad", dq, ds, d["wq3"], d["ws3"]))
             dqt, dst, _ = tm.region("wgrad.quant_dy", lambda: fp8.quant_act_1x128(d["dy4"], "col"))
             xqt, xst, _ = tm.region("wgrad.quant_x", lambda: fp8.quant_act_1x128(d["x3"], "col"))
             tm.region("wgrad.gemm", lambda: fp8.block_gemm("wgrad", dqt, dst, xqt, xst,
@@ -221,7 +223,7 @@ def main():
             ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
             tm.pending.append(("grouped", ev0, ev1))
         if want("weights"):
-            tm.region("weights", lambda: fp8.quant_weight_128x128(d["w3"], transposed=False))
+            tm.region("weights", lambda: fp8.quant_weight_128x128(d["w3"], transposed=True))
         if want("policy"):
             def pol():
                 fp8.quant_act_1x128(d["xp"], "row", scales_in=d["sp"], return_amax=True,
@@ -277,7 +279,9 @@ def main():
         tq1, tg1 = tm.mean_ms("dgrad.quant"), tm.mean_ms("dgrad.gemm")
         tq2, tq3, tg2 = tm.mean_ms("wgrad.quant_dy"), tm.mean_ms("wgrad.quant_x"), tm.mean_ms("wgrad.gemm")
         rows["dgrad"] = {"ms_quant": tq1, "ms_gemm": tg1, "TFLOP/s_incl_quant": F3 / (tq1 + tg1) / 1e9,
-                         "TFLOP/s_gemm": F3 / tg1 / 1e9}
+                         "TFLOP/s_gemm": F3 / tg1 / 1e9, "layout": "dgrad_t (W_q^T)"}
+        tl = tm.mean_ms("dgrad_lds.gemm")
+        rows["dgrad_lds"] = {"ms_gemm": tl, "TFLOP/s_gemm": F3 / tl / 1e9, "layout": "dgrad (W_q read transposed)"}
         rows["wgrad"] = {"ms_quant_dy_col": tq2, "ms_quant_x_col": tq3, "ms_gemm": tg2,
                          "TFLOP/s_incl_quant": F3 / (tq2 + tq3 + tg2) / 1e9, "TFLOP/s_gemm": F3 / tg2 / 1e9,
                          "col_quant_GB/s": (4096 * 18432 + 4096 * 7168) * (3 + 4 / 128) / (tq2 + tq3) / 1e6}
@@ -287,7 +291,7 @@ def main():
         rows["grouped"] = {"ms_quant": tq, "ms_gemm": tg, "TFLOP/s_incl_quant": F5 / (tq + tg) / 1e9,
                            "TFLOP/s_gemm": F5 / tg / 1e9, "tokens_per_expert": [int(c) for c in d["counts5"]]}
     if want("weights"):
-        B = 18432 * 7168 * 3 + (18432 // 128) * (7168 // 128) * 4
+        B = 18432 * 7168 * 4 + (18432 // 128) * (7168 // 128) * 4
         t = tm.mean_ms("weights")
         rows["weights"] = {"ms": t, "GB/s": B / t / 1e6}
     if want("policy"):

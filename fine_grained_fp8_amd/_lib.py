@@ -17,7 +17,7 @@ STATUS = {
     5: "FP8_ERR_UNSUPPORTED", 6: "FP8_ERR_DEVICE", 7: "FP8_ERR_LAUNCH", 8: "FP8_ERR_ALIAS",
 }
 TILE_ROW, TILE_COL = 0, 1
-LAYOUT = {"fprop": 0, "dgrad": 1, "wgrad": 2}
+LAYOUT = {"fprop": 0, "dgrad": 1, "wgrad": 2, "dgrad_t": 3}
 OUT_BF16, OUT_FP32 = 0, 1
 
 # name -> (restype, argtypes); mirrors include/fp8bs.h

@@ -170,7 +170,8 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
                           const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
                           const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
                           void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream) {
-  if (layout != FP8_LAYOUT_FPROP && layout != FP8_LAYOUT_DGRAD && layout != FP8_LAYOUT_WGRAD)
+  if (layout != FP8_LAYOUT_FPROP && layout != FP8_LAYOUT_DGRAD && layout != FP8_LAYOUT_WGRAD &&
+      layout != FP8_LAYOUT_DGRAD_T)
     return FP8_ERR_UNSUPPORTED;
   fp8_status st = validate_gemm_common(M, N, K, A, lda, sA, ld_sa, B, sB, C, c_dtype, ldc);
   if (st != FP8_OK || M == 0) return st;
@@ -179,6 +180,7 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
   switch (layout) {
     case FP8_LAYOUT_FPROP: b_rows = N; b_cols = K; sb_rows = N / 128; sb_cols = K / 128; break;
     case FP8_LAYOUT_DGRAD: b_rows = K; b_cols = N; sb_rows = K / 128; sb_cols = N / 128; break;
+    case FP8_LAYOUT_DGRAD_T: b_rows = N; b_cols = K; sb_rows = K / 128; sb_cols = N / 128; break;
     default: b_rows = N; b_cols = K; sb_rows = K / 128; sb_cols = N; break;
   }
   if (ldb < b_cols || ld_sb < sb_cols) return FP8_ERR_LD;

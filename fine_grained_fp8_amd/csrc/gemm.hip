@@ -498,12 +498,18 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
       (void*)(Bp + n0 * p.ldb), (short)0, rows_n * (int)p.ldb, (int)kRsrcWord3);
   const uint32_t off_w = (uint32_t)((wave * 64 + lrow) * (int)p.ldb + lgrp * 16);
   const uint32_t w_istride = (uint32_t)(16 * p.ldb);
-  // weight-side scales: Fprop - the wave's 128x128 weight block (every lane
-  // fetches the same float); Wgrad - the workgroup's 256 per-column scales
-  const int64_t sw_elems = kLayout == kFprop ? (p.N / 128) * p.ld_sb : 0;
+  // weight-side scales: Fprop / Dgrad_T - the wave's 128x128 weight block
+  // (every lane fetches the same float; Fprop's table is [N/128][K/128],
+  // Dgrad_T reads the forward table [K/128][N/128]); Wgrad - the workgroup's
+  // 256 per-column scales
+  constexpr bool kBlockW = kLayout == kFprop || kLayout == kDgradT;
+  const int64_t sw_elems = kLayout == kFprop ? (p.N / 128) * p.ld_sb
+                                             : (kLayout == kDgradT ? (p.K / BK) * p.ld_sb : 0);
   const __amdgpu_buffer_rsrc_t rsrc_sw = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)sBp, (short)0, kLayout == kFprop ? (int)(sw_elems * 4) : 0, (int)kRsrcWord3);
-  const uint32_t sw_off = (uint32_t)(((n0 + 64 * wave) / 128) * p.ld_sb) * 4u;
+      (void*)sBp, (short)0, (int)(sw_elems * 4), (int)kRsrcWord3);
+  const int64_t nbw = (n0 + 64 * wave) / 128;
+  const uint32_t sw_off = kLayout == kFprop ? (uint32_t)(nbw * p.ld_sb) * 4u : (uint32_t)nbw * 4u;
+  const uint32_t sw_kstride = kLayout == kFprop ? 4u : (uint32_t)p.ld_sb * 4u;
 
   auto issue_load = [&](int kb, int op, uint8_t* st, v8i (&wr)[DNI]) {
     if (op < 4) {
@@ -520,7 +526,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + kDWScaleOff), 16, (uint32_t)(lane * 16), 0, 0, 0);
       } else {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_sw, (lds_ptr_t)(st + kDWScaleOff + wave * 256), 4,
-                                                 sw_off + (uint32_t)kb * 4u, 0, 0, 0);
+                                                 sw_off + (uint32_t)kb * sw_kstride, 0, 0, 0);
       }
     } else {
       const int i = (op - 6) >> 1, h = (op - 6) & 1;
@@ -569,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     const float* sxl = reinterpret_cast<const float*>(st + kDScaleOff);
     const float* swl = reinterpret_cast<const float*>(st + kDWScaleOff);
     float wsc = 1.f;
-    if constexpr (kLayout == kFprop) wsc = swl[wave * 64];
+    if constexpr (kBlockW) wsc = swl[wave * 64];
     // scales first: their LDS reads complete ahead of the operand reads, so
     // the waits for them do not wait for the operands
     float c[DNJ];
@@ -722,6 +728,7 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
   switch (p.layout) {
     case kFprop: return launch_typed<kFprop, false>(p, stream, total, total);
     case kDgrad: return launch_typed<kDgrad, false>(p, stream, total, total);
+    case kDgradT: return launch_typed<kDgradT, false>(p, stream, total, total);
     default: return launch_typed<kWgrad, false>(p, stream, total, total);
   }
 }

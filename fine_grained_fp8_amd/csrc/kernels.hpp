@@ -26,7 +26,7 @@ hipError_t launch_history_update(float* hist, const float* amax, int64_t n, floa
 
 hipError_t launch_cast_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream);
 
-enum GemmLayout { kFprop = 0, kDgrad = 1, kWgrad = 2 };
+enum GemmLayout { kFprop = 0, kDgrad = 1, kWgrad = 2, kDgradT = 3 };
 
 struct GemmProblem {
   int layout;            // GemmLayout
@@ -35,7 +35,7 @@ struct GemmProblem {
   int64_t lda;
   const float* sA;       // [K/128][ld_sa]
   int64_t ld_sa;
-  const uint8_t* B;      // weight side: [N][K] (FPROP, WGRAD) or [K][N] (DGRAD)
+  const uint8_t* B;      // weight side: [N][K] (FPROP, WGRAD, DGRAD_T) or [K][N] (DGRAD)
   int64_t ldb;
   const float* sB;
   int64_t ld_sb;

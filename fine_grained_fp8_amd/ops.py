@@ -111,6 +111,8 @@ def block_gemm(layout: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, 
 
     fprop: A [M][K], sA [K/128][>=M], B [N][K], sB [N/128][>=K/128]
     dgrad: A [M][K], sA [K/128][>=M], B [K][N] (forward W_q), sB [K/128][>=N/128]
+    dgrad_t: A [M][K], sA [K/128][>=M], B [N][K] (W_q^T, the q_t of the weight
+             quantizer), sB [K/128][>=N/128] (the forward block-scale table)
     wgrad: A [M][K], sA [K/128][>=M], B [N][K], sB [K/128][>=N]
     Returns C [M][N] in out_dtype (bfloat16 or float32).
     """

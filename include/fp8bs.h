@@ -84,7 +84,8 @@ typedef enum {
 typedef enum {
   FP8_LAYOUT_FPROP = 0, /* C[M][N] = A[M][K] . B[N][K]^T,  B = W_q (weights [d_out][d_in]) */
   FP8_LAYOUT_DGRAD = 1, /* C[M][N] = A[M][K] . B[K][N],    B = W_q stored [d_out = K][d_in = N] */
-  FP8_LAYOUT_WGRAD = 2  /* C[M][N] = A[M][K] . B[N][K]^T,  K = tokens, per-row x per-column scales */
+  FP8_LAYOUT_WGRAD = 2, /* C[M][N] = A[M][K] . B[N][K]^T,  K = tokens, per-row x per-column scales */
+  FP8_LAYOUT_DGRAD_T = 3 /* C[M][N] = A[M][K] . B[N][K]^T,  B = W_q^T (transposed weight codes) */
 } fp8_gemm_layout;
 
 typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_FP32 = 1 } fp8_out_dtype;
@@ -150,6 +151,12 @@ fp8_status fp8_quant_weight_128x128(const void* w, int64_t rows, int64_t cols, i
  *     B  = W_q  stored [K][ldb >= N] and contracted over its rows (the forward
  *          weight codes, read transposed in the kernel);
  *     sB = the same block-scale table, [K/128][ld_sb >= N/128].
+ *     N % 128 == 0.
+ *  FP8_LAYOUT_DGRAD_T (M = tokens, N = d_in, K = d_out) - Dgrad from the
+ *                     transposed weight codes, same result as FP8_LAYOUT_DGRAD
+ *     A  = dY_q  [M][lda >= K];    sA [K/128][ld_sa >= M]     (1x128 row scales)
+ *     B  = W_q^T [N][ldb >= K]     (q_t of fp8_quant_weight_128x128);
+ *     sB = the forward block-scale table, [K/128][ld_sb >= N/128].
  *     N % 128 == 0.
  *  FP8_LAYOUT_WGRAD   (M = d_out, N = d_in, K = tokens)
  *     A  = dY_q^T [M][lda >= K];   sA [K/128][ld_sa >= M]     (128x1 column scales)

@@ -142,6 +142,46 @@ def test_dgrad_full_size_sampled(gpu_lib, big_layer):
     check_gemm(bf16_bits(C)[rows], R, T, 18432, E=E, label="dgrad 4096x7168x18432")
 
 
+def run_dgrad_t(fp8, dYq, s_dY, Wq_t, sW):
+    C = fp8.block_gemm("dgrad_t", dev(dYq), act_scales_dev(s_dY), dev(Wq_t), dev(sW))
+    torch.cuda.synchronize()
+    return C
+
+
+def test_dgrad_t_small_with_gpu_transposed_codes(gpu_lib):
+    """Dgrad from W_q^T: the weight quantizer's transposed codes feed the
+    Fprop-shaped kernel with the forward scale table read transposed."""
+    dyb = syn.gaussian((200, 384), seed=31, std=1e-3)          # [tokens][d_out]
+    wb = syn.gaussian((384, 256), seed=32, std=0.02)            # W [d_out][d_in]
+    dYq, s_dY = quant.quant_rows(dyb)
+    Wq, sW = quant.quant_weight(wb)
+    q, s, q_t = gpu_lib.quant_weight_128x128(dev(wb), transposed=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(q_t.cpu().numpy(), np.ascontiguousarray(Wq.T))
+    R, T = og.dgrad(dYq, s_dY, Wq, sW, with_magnitude=True)
+    E = truncation_bound(dYq, s_dY, np.ascontiguousarray(Wq.T), og.expand_block_scales(sW.T, 256))
+    C = gpu_lib.block_gemm("dgrad_t", dev(dYq), act_scales_dev(s_dY), q_t, s)
+    torch.cuda.synchronize()
+    check_gemm(bf16_bits(C), R, T, 384, E=E, label="dgrad_t small")
+    # the same kernel as Fprop on the explicitly transposed weights and scales
+    F = run_fprop(gpu_lib, dYq, s_dY, np.ascontiguousarray(Wq.T), np.ascontiguousarray(sW.T))
+    assert torch.equal(C.view(torch.int16), F.view(torch.int16))
+
+
+def test_dgrad_t_full_size_sampled(gpu_lib, big_layer):
+    _, _, Wq, sW = big_layer
+    dyb = syn.gaussian((4096, 18432), seed=4, std=1e-3)
+    dYq, s_dY = quant.quant_rows(dyb)
+    del dyb
+    C = run_dgrad_t(gpu_lib, dYq, s_dY, np.ascontiguousarray(Wq.T), sW)
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 4, replace=False)]))
+    R, T = og.dgrad(dYq[rows], s_dY[rows], Wq, sW, with_magnitude=True)
+    E = truncation_bound(dYq[rows], s_dY[rows], np.ascontiguousarray(Wq.T),
+                         og.expand_block_scales(np.ascontiguousarray(sW.T), 7168))
+    check_gemm(bf16_bits(C)[rows], R, T, 18432, E=E, label="dgrad_t 4096x7168x18432")
+
+
 def run_wgrad(fp8, dYt, s_dy, Xt, s_x, out_dtype=torch.float32):
     C = fp8.block_gemm("wgrad", dev(dYt), act_scales_dev(s_dy), dev(Xt), act_scales_dev(s_x),
                        out_dtype=out_dtype)

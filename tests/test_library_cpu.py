@@ -103,7 +103,8 @@ def gemm(lib, layout=0, M=256, N=256, K=512, a=A, lda=512, sa=S, ld_sa=256, b=B,
 
 
 def test_gemm_validation(lib):
-    assert gemm(lib, layout=3) == UNSUP
+    assert gemm(lib, layout=4) == UNSUP
+    assert gemm(lib, layout=-1) == UNSUP
     assert gemm(lib, dt=5) == UNSUP
     assert gemm(lib, K=200, lda=256) == SHAPE
     assert gemm(lib, K=0) == SHAPE
@@ -119,6 +120,11 @@ def test_gemm_validation(lib):
     # DGRAD: B stored [K][N], block scales [K/128][N/128]
     assert gemm(lib, layout=1, ldb=128, ld_sb=2) == LD
     assert gemm(lib, layout=1, ldb=256, ld_sb=1) == LD
+    # DGRAD_T: B = W_q^T [N][K], the forward block scales [K/128][N/128]
+    assert gemm(lib, layout=3, N=200, ldc=256) == SHAPE
+    assert gemm(lib, layout=3, ldb=256) == LD
+    assert gemm(lib, layout=3, ld_sb=1) == LD
+    assert gemm(lib, layout=3, ld_sb=2) in (DEVICE, OK)
     # WGRAD: any N, column scales [K/128][N]
     assert gemm(lib, layout=2, N=200, ldc=208, ld_sb=150) == LD
     assert gemm(lib, layout=2, N=200, ldc=208, ld_sb=200, dt=1) in (DEVICE, OK)

@@ -12,6 +12,11 @@
 #include "device.hpp"
 #include "kernels.hpp"
 
+namespace {
+typedef int sv4i __attribute__((ext_vector_type(4)));
+typedef int sv2i __attribute__((ext_vector_type(2)));
+}  // namespace
+
 namespace fp8bs {
 
 // ---------------------------------------------------------------------------
@@ -39,11 +44,16 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   const int64_t r0 = rb * kRows;
   const uint16_t* xb = x + kb * 128 + l16 * 8;
 
+  // The input is read once and the codes are written once: streaming
+  // (non-temporal) accesses keep them from displacing cached data, which
+  // measured ~6% faster with the input streamed from HBM.
   uint4 v[kG];
 #pragma unroll
   for (int g = 0; g < kG; ++g) {
     const int64_t row = r0 + 4 * g + sub;
-    v[g] = row < rows ? *reinterpret_cast<const uint4*>(xb + row * ldx) : make_uint4(0, 0, 0, 0);
+    const sv4i t = row < rows ? __builtin_nontemporal_load(reinterpret_cast<const sv4i*>(xb + row * ldx))
+                              : sv4i{0, 0, 0, 0};
+    v[g] = make_uint4((uint32_t)t[0], (uint32_t)t[1], (uint32_t)t[2], (uint32_t)t[3]);
   }
 
   float my_s = 0.0f, my_amax = 0.0f;
@@ -82,7 +92,9 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
         }
       }
     }
-    if (row < rows) *reinterpret_cast<uint2*>(q + row * ldq + kb * 128 + l16 * 8) = out;
+    if (row < rows)
+      __builtin_nontemporal_store(sv2i{(int)out.x, (int)out.y},
+                                  reinterpret_cast<sv2i*>(q + row * ldq + kb * 128 + l16 * 8));
     // lane j collects the scale of row r0 + j, held by lane 16 * (j % 4) in group j / 4
     const float sg = __shfl(s, (lane & 3) * 16);
     const float ag = __shfl(amax_value(t), (lane & 3) * 16);

@@ -6,10 +6,12 @@ seeded synthetic inputs already resident in HBM:
   quantizer  1x128 online quantization of X 8192x7168 (outliers in 16 channels)
   fprop      1x128 quantization of X 4096x7168 + block-scaled GEMM
              Y = X W^T 4096x18432x7168 (W pre-quantized 128x128), BF16 out
-  backward   dY 4096x18432: 1x128 quantization + Dgrad dX = dY W from the
-             transposed weight codes W_q^T; 128x1 quantization of dY and X +
+  backward   dY 4096x18432 quantized in both orientations from one read
+             (1x128 rows for Dgrad, 128x1 columns for Wgrad); Dgrad dX = dY W
+             from the transposed weight codes W_q^T; 128x1 quantization of X +
              Wgrad dW = dY^T X (FP32 out).  Also reported: Dgrad reading W_q
-             as stored (transposed in LDS), "dgrad_lds".
+             as stored ("dgrad_lds") and the dY quantization as two separate
+             passes ("dual_quant")
   grouped    1x128 quantization of X 16384x7168 + one grouped launch over 8
              experts (multinomial token counts), W_e 2048x7168
   weights    128x128 quantization of W 18432x7168 with the transposed copy
@@ -207,15 +209,18 @@ def main():
             tm.pending.append(("fprop", ev0, ev1))
         if want("backward"):
             ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
-            dq, ds, _ = tm.region("dgrad.quant", lambda: fp8.quant_act_1x128(d["dy4"], "row"))
+            # dY in both orientations from one read (Dgrad rows, Wgrad columns)
+            dq, ds, dqt, dst = tm.region("bwd.quant_dual", lambda: fp8.quant_act_dual(d["dy4"]))
             tm.region("dgrad.gemm", lambda: fp8.block_gemm("dgrad_t", dq, ds, d["wq3t"], d["ws3"]))
             tm.region("dgrad_lds.gemm", lambda: fp8.block_gemm("dgrad", dq, ds, d["wq3"], d["ws3"]))
-            dqt, dst, _ = tm.region("wgrad.quant_dy", lambda: fp8.quant_act_1x128(d["dy4"], "col"))
             xqt, xst, _ = tm.region("wgrad.quant_x", lambda: fp8.quant_act_1x128(d["x3"], "col"))
             tm.region("wgrad.gemm", lambda: fp8.block_gemm("wgrad", dqt, dst, xqt, xst,
                                                            out_dtype=torch.float32))
             ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
             tm.pending.append(("backward", ev0, ev1))
+            # the same two quantizations as separate passes, for comparison
+            tm.region("bwd.quant_row", lambda: fp8.quant_act_1x128(d["dy4"], "row"))
+            tm.region("bwd.quant_col", lambda: fp8.quant_act_1x128(d["dy4"], "col"))
         if want("grouped"):
             ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
             q, s, _ = tm.region("grouped.quant", lambda: fp8.quant_act_1x128(d["x5"], "row"))
@@ -308,15 +313,23 @@ def main():
                     "algorithmic_flop_per_launch": F3, "ms_per_launch": batch["fprop.gemm"],
                     "timing": "5 back-to-back launches between HIP events on the launch stream"}
     if want("backward"):
-        tq1, tg1 = tm.mean_ms("dgrad.quant"), tm.mean_ms("dgrad.gemm")
-        tq2, tq3, tg2 = tm.mean_ms("wgrad.quant_dy"), tm.mean_ms("wgrad.quant_x"), tm.mean_ms("wgrad.gemm")
-        rows["dgrad"] = {"ms_quant": tq1, "ms_gemm": tg1, "TFLOP/s_incl_quant": F3 / (tq1 + tg1) / 1e9,
+        tdual, tg1 = tm.mean_ms("bwd.quant_dual"), tm.mean_ms("dgrad.gemm")
+        tq3, tg2 = tm.mean_ms("wgrad.quant_x"), tm.mean_ms("wgrad.gemm")
+        trow, tcol = tm.mean_ms("bwd.quant_row"), tm.mean_ms("bwd.quant_col")
+        EL = 4096 * 18432
+        rows["dual_quant"] = {"ms": tdual, "GB/s": EL * (2 + 2 + 8 / 128) / tdual / 1e6,
+                              "ms_separate_row_plus_col": trow + tcol,
+                              "GB/s_separate": EL * 2 * (3 + 4 / 128) / (trow + tcol) / 1e6,
+                              "speedup_vs_separate": (trow + tcol) / tdual}
+        # each GEMM is charged the share of the dual pass its operand costs
+        tq1 = tq2 = tdual / 2
+        rows["dgrad"] = {"ms_quant_share": tq1, "ms_gemm": tg1, "TFLOP/s_incl_quant": F3 / (tq1 + tg1) / 1e9,
                          "TFLOP/s_gemm": F3 / tg1 / 1e9, "layout": "dgrad_t (W_q^T)"}
         tl = tm.mean_ms("dgrad_lds.gemm")
         rows["dgrad_lds"] = {"ms_gemm": tl, "TFLOP/s_gemm": F3 / tl / 1e9, "layout": "dgrad (W_q read transposed)"}
-        rows["wgrad"] = {"ms_quant_dy_col": tq2, "ms_quant_x_col": tq3, "ms_gemm": tg2,
+        rows["wgrad"] = {"ms_quant_dy_share": tq2, "ms_quant_x_col": tq3, "ms_gemm": tg2,
                          "TFLOP/s_incl_quant": F3 / (tq2 + tq3 + tg2) / 1e9, "TFLOP/s_gemm": F3 / tg2 / 1e9,
-                         "col_quant_GB/s": (4096 * 18432 + 4096 * 7168) * (3 + 4 / 128) / (tq2 + tq3) / 1e6}
+                         "col_quant_x_GB/s": 4096 * 7168 * (3 + 4 / 128) / tq3 / 1e6}
     if want("grouped"):
         F5 = 2.0 * 16384 * 2048 * 7168
         tq, tg = tm.mean_ms("grouped.quant"), tm.mean_ms("grouped.gemm")

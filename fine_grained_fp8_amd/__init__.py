@@ -9,6 +9,7 @@ fail loudly when the library is missing.
 from ._lib import FP8Error, load_library, LIB_PATH, SIGNATURES  # noqa: F401
 from .ops import (  # noqa: F401
     quant_act_1x128,
+    quant_act_dual,
     quant_weight_128x128,
     block_gemm,
     block_gemm_grouped,
@@ -18,6 +19,6 @@ from .ops import (  # noqa: F401
 )
 
 __all__ = [
-    "FP8Error", "load_library", "quant_act_1x128", "quant_weight_128x128", "block_gemm",
+    "FP8Error", "load_library", "quant_act_1x128", "quant_act_dual", "quant_weight_128x128", "block_gemm",
     "block_gemm_grouped", "amax_history_update", "cast_e4m3", "round_up",
 ]

@@ -28,6 +28,8 @@ _F = ctypes.c_float
 SIGNATURES = {
     "fp8_quant_act_1x128": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int, _P, _I64, _P, _I64,
                                            _P, _P, _P, _P]),
+    "fp8_quant_act_dual": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
+                                          _P]),
     "fp8_quant_weight_128x128": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
     "fp8_block_gemm": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P,
                                       _I64, _P, ctypes.c_int, _I64, _P]),

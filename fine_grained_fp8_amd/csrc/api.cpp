@@ -123,6 +123,36 @@ fp8_status fp8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_
   return launched(fp8bs::launch_quant_cols(xb, rows, cols, ldx, q, ldq, scales, ld_s, amax_out, st));
 }
 
+fp8_status fp8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                              uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t ld_s_row,
+                              uint8_t* q_col, int64_t ldq_col, float* s_col, int64_t ld_s_col,
+                              void* stream) {
+  if (rows < 0 || cols < 0 || rows % 128 != 0 || cols % 128 != 0) return FP8_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8_OK;
+  if (!x || !q_row || !s_row || !q_col || !s_col) return FP8_ERR_NULL;
+  if (ldx < cols || ldq_row < cols || ld_s_row < rows || ldq_col < rows || ld_s_col < cols)
+    return FP8_ERR_LD;
+  if (!aligned16(x) || !aligned16(q_row) || !aligned16(q_col) || (ldx * 2) % 16 != 0 ||
+      ldq_row % 16 != 0 || ldq_col % 16 != 0 || !aligned4(s_row) || !aligned4(s_col))
+    return FP8_ERR_ALIGN;
+  const Range rx = span(x, rows, cols * 2, ldx * 2);
+  const Range rqr = span(q_row, rows, cols, ldq_row);
+  const Range rsr = span(s_row, cols / 128, rows * 4, ld_s_row * 4);
+  const Range rqc = span(q_col, cols, rows, ldq_col);
+  const Range rsc = span(s_col, rows / 128, cols * 4, ld_s_col * 4);
+  const Range outs[4] = {rqr, rsr, rqc, rsc};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], rx)) return FP8_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return FP8_ERR_ALIAS;
+  }
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  return launched(fp8bs::launch_quant_dual(static_cast<const uint16_t*>(x), rows, cols, ldx, q_row,
+                                           ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col, ld_s_col,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
 fp8_status fp8_quant_weight_128x128(const void* w, int64_t rows, int64_t cols, int64_t ldw,
                                     uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
                                     float* scales, int64_t ld_s, void* stream) {

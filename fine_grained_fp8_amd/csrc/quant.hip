@@ -197,6 +197,105 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Both orientations of the backward-pass activation from one read: for a
+// 128x128 block, the 1x128 row tiles (Dgrad operand, row-major codes and
+// MN-major scales) and the 128x1 column tiles (Wgrad operand, transposed
+// codes).  The row tiles are quantized from registers exactly as in
+// quant_rows_kernel (one 16-lane DPP row per tile row); the block is also
+// staged in LDS, where each thread takes two adjacent columns x 32 rows and
+// the column max is combined across the four row segments.  Every code and
+// scale equals the one the separate row and column quantizers produce.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_dual_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t ncb,
+    uint8_t* __restrict__ q_row, int64_t ldq_row, float* __restrict__ s_row, int64_t ld_s_row,
+    uint8_t* __restrict__ q_col, int64_t ldq_col, float* __restrict__ s_col, int64_t ld_s_col) {
+  __shared__ uint32_t tile[128][64];   // BF16 pairs: word c holds columns 2c, 2c+1
+  __shared__ uint32_t red[4][64];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int sub = lane >> 4, l16 = lane & 15;
+  const int64_t rb = blockIdx.x / ncb;
+  const int64_t kb = blockIdx.x % ncb;
+  const int64_t r0 = rb * 128, c0 = kb * 128;
+
+  // ---- load: row wave*32 + 4i + sub, 8 BF16 at columns 8*l16.. ----
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = wave * 32 + 4 * i + sub;
+    v[i] = *reinterpret_cast<const uint4*>(x + (r0 + row) * ldx + c0 + l16 * 8);
+    *reinterpret_cast<uint4*>(&tile[row][l16 * 4]) = v[i];
+  }
+
+  // ---- 1x128 row tiles, from registers ----
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = wave * 32 + 4 * i + sub;
+    const uint32_t ta = row16_max_u32(absmax_bits8(v[i]));
+    const float s = tile_scale(ta);
+    const uint4 d = v[i];
+    uint2 out;
+    if (ta < kBf16InfAbs) {
+      const float r = 1.0f / s;
+      out.x = pack4_sat(div_by_scale(bf16_lo(d.x), s, r), div_by_scale(bf16_hi(d.x), s, r),
+                        div_by_scale(bf16_lo(d.y), s, r), div_by_scale(bf16_hi(d.y), s, r));
+      out.y = pack4_sat(div_by_scale(bf16_lo(d.z), s, r), div_by_scale(bf16_hi(d.z), s, r),
+                        div_by_scale(bf16_lo(d.w), s, r), div_by_scale(bf16_hi(d.w), s, r));
+    } else {
+      out.x = pack4_sat_nan(bf16_lo(d.x) / s, bf16_hi(d.x) / s, bf16_lo(d.y) / s, bf16_hi(d.y) / s);
+      out.y = pack4_sat_nan(bf16_lo(d.z) / s, bf16_hi(d.z) / s, bf16_lo(d.w) / s, bf16_hi(d.w) / s);
+    }
+    *reinterpret_cast<uint2*>(q_row + (r0 + row) * ldq_row + c0 + l16 * 8) = out;
+    if (l16 == 0) s_row[kb * ld_s_row + r0 + row] = s;
+  }
+  __syncthreads();
+
+  // ---- 128x1 column tiles, from LDS: columns 2p, 2p+1, rows seg*32.. ----
+  const int p = t & 63, seg = t >> 6;
+  uint32_t d[32];
+  us2 m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    d[i] = tile[seg * 32 + i][p];
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[i] & 0x7FFF7FFFu));
+  }
+  red[seg][p] = __builtin_bit_cast(uint32_t, m);
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < 4; ++g) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, red[g][p]));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t tt = h ? m.y : m.x;
+    const float s = tile_scale(tt);
+    uint32_t w[8];
+    if (tt < kBf16InfAbs) {
+      const float r = 1.0f / s;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = div_by_scale(h ? bf16_hi(d[4 * k + e]) : bf16_lo(d[4 * k + e]), s, r);
+        w[k] = pack4_sat(y[0], y[1], y[2], y[3]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (h ? bf16_hi(d[4 * k + e]) : bf16_lo(d[4 * k + e])) / s;
+        w[k] = pack4_sat_nan(y[0], y[1], y[2], y[3]);
+      }
+    }
+    const int64_t col = c0 + 2 * p + h;
+    uint4* dst = reinterpret_cast<uint4*>(q_col + col * ldq_col + r0 + seg * 32);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    if (seg == 0) s_col[rb * ld_s_col + col] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 128x128 weight blocks: one workgroup per block, block max through DPP row
 // reduction, cross-row shuffles and LDS; optional transposed codes via an LDS
 // byte tile and 4x4 byte transposes (for the input-gradient GEMM).
@@ -318,6 +417,17 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
     hipLaunchKernelGGL((quant_rows_kernel<false, kG>), dim3((unsigned)nblocks), dim3(256), 0, stream,
                        x, rows, ldx, kblocks, q, ldq, scales, ld_s, scales_in, amax_out, sat_count);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t ld_s_row,
+                             uint8_t* q_col, int64_t ldq_col, float* s_col, int64_t ld_s_col,
+                             hipStream_t stream) {
+  const int64_t ncb = cols / 128;
+  const int64_t nblocks = (rows / 128) * ncb;
+  hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, x, ldx, ncb,
+                     q_row, ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col, ld_s_col);
   return hipGetLastError();
 }
 

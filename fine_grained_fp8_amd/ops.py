@@ -87,6 +87,27 @@ def quant_act_1x128(x: torch.Tensor, direction: str = "row", *, scales_in=None,
     return q, scales, amax
 
 
+def quant_act_dual(x: torch.Tensor, *, stream=None):
+    """Both orientations of x [rows][cols] BF16 from one read.
+
+    Returns (q_row [rows][cols], s_row [cols/128][round_up(rows, 4)],
+             q_col [cols][rows], s_col [rows/128][round_up(cols, 4)]) - the outputs of
+    quant_act_1x128(x, "row") and quant_act_1x128(x, "col").
+    """
+    lib = _lib.load_library()
+    _check_2d("x", x, _BF16)
+    rows, cols = x.shape
+    q_row = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s_row = torch.empty((cols // 128, round_up(rows, 4)), dtype=torch.float32, device=x.device)
+    q_col = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    s_col = torch.empty((rows // 128, round_up(cols, 4)), dtype=torch.float32, device=x.device)
+    st = lib.fp8_quant_act_dual(_ptr(x), rows, cols, x.stride(0), _ptr(q_row), q_row.stride(0),
+                                _ptr(s_row), s_row.stride(0), _ptr(q_col), q_col.stride(0),
+                                _ptr(s_col), s_col.stride(0), _stream(stream))
+    _lib.check("fp8_quant_act_dual", st)
+    return q_row, s_row, q_col, s_col
+
+
 def quant_weight_128x128(w: torch.Tensor, *, transposed: bool = False, stream=None):
     """128x128 block quantization of weights [N][K].
 

@@ -124,6 +124,28 @@ fp8_status fp8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_
                                float* amax_out, uint32_t* sat_count, void* stream);
 
 /*
+ * fp8_quant_act_dual - both orientations of a backward-pass activation from
+ * one read of it: the 1x128 row tiles that Dgrad consumes and the 128x1
+ * column tiles, transposed, that Wgrad consumes.  The outputs are exactly
+ * those of fp8_quant_act_1x128 with FP8_TILE_ROW and with FP8_TILE_COL
+ * (online scales).  One read of x instead of two ("Online Quantization
+ * During Training" section 5: separate passes move the tensor through memory
+ * again and again; "Fine-Grained FP8 Quantization in DeepSeek" section 4:
+ * the transpose layout decides real performance).
+ *
+ *  x      BF16 [rows][ldx >= cols]; rows % 128 == 0 and cols % 128 == 0.
+ *  q_row  [rows][ldq_row >= cols]          row-tile codes
+ *  s_row  [cols/128][ld_s_row >= rows]     row-tile scales (MN-major)
+ *  q_col  [cols][ldq_col >= rows]          column-tile codes, transposed
+ *  s_col  [rows/128][ld_s_col >= cols]     column-tile scales
+ *  No output may overlap x or another output.
+ */
+fp8_status fp8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                              uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t ld_s_row,
+                              uint8_t* q_col, int64_t ldq_col, float* s_col, int64_t ld_s_col,
+                              void* stream);
+
+/*
  * fp8_quant_weight_128x128 - 128x128 weight-block quantization, blocks
  * anchored at (0, 0); same per-block rule as above over 16384 values.
  *

@@ -154,6 +154,69 @@ def test_quant_cols_full_size_sampled(gpu_lib):
     assert_cols_match(gpu_lib, x, cols_idx=cols, label="dY col 4096x18432")
 
 
+def assert_dual_match(fp8, x_bits, label=""):
+    """fp8_quant_act_dual = the oracle's row and column quantizations, bit for bit,
+    and = the two separate GPU quantizations."""
+    M, C = x_bits.shape
+    xt = dev(x_bits)
+    q_row, s_row, q_col, s_col = fp8.quant_act_dual(xt)
+    qr, sr, _ = fp8.quant_act_1x128(xt, "row")
+    qc, sc, _ = fp8.quant_act_1x128(xt, "col")
+    torch.cuda.synchronize()
+    assert torch.equal(q_row, qr) and torch.equal(q_col, qc), f"{label}: codes differ from separate passes"
+    assert torch.equal(s_row[:, :M].view(torch.int32), sr[:, :M].view(torch.int32)), label
+    assert torch.equal(s_col[:, :C].view(torch.int32), sc[:, :C].view(torch.int32)), label
+    q_o, s_o = quant.quant_rows(x_bits)
+    assert np.array_equal(host(q_row), q_o), f"{label}: row codes differ from the oracle"
+    assert np.array_equal(scale_bits(host(s_row)[:, :M].T), scale_bits(s_o)), f"{label}: row scales"
+    qc_o, sc_o = quant.quant_cols(x_bits)
+    assert np.array_equal(host(q_col), qc_o), f"{label}: column codes differ from the oracle"
+    assert np.array_equal(scale_bits(host(s_col)[:, :C].T), scale_bits(sc_o)), f"{label}: column scales"
+
+
+@pytest.mark.parametrize("case", ["gauss", "outliers", "adversarial", "lossless_rows", "lossless_cols"])
+def test_quant_dual_small(gpu_lib, case):
+    if case == "gauss":
+        x = syn.gaussian((256, 384), seed=12, std=1e-3)
+    elif case == "outliers":
+        x = syn.activation_with_outliers(384, 256, seed=13)
+    elif case == "adversarial":
+        # special-value tiles both along rows and, transposed, along columns
+        a = adversarial_rows()                          # [12][256]
+        x = np.zeros((256, 256), np.uint16)
+        x[:a.shape[0], :] = a
+        x[:, 128:128 + a.shape[0]] = a.T
+    elif case == "lossless_rows":
+        x, _ = syn.lossless_tiles(256, 256, seed=14, tile=(1, 128))
+    else:
+        x, _ = syn.lossless_tiles(256, 256, seed=15, tile=(128, 1))
+    assert_dual_match(gpu_lib, x, label=case)
+
+
+def test_quant_dual_full_size(gpu_lib):
+    """dY 4096x18432: both orientations equal the separate passes everywhere
+    (compared on the GPU) and the oracle on a sample of rows and columns."""
+    M, C = 4096, 18432
+    x = syn.gaussian((M, C), seed=4, std=1e-3)
+    xt = dev(x)
+    q_row, s_row, q_col, s_col = gpu_lib.quant_act_dual(xt)
+    qr, sr, _ = gpu_lib.quant_act_1x128(xt, "row")
+    qc, sc, _ = gpu_lib.quant_act_1x128(xt, "col")
+    torch.cuda.synchronize()
+    assert torch.equal(q_row, qr) and torch.equal(q_col, qc)
+    assert torch.equal(s_row[:, :M].view(torch.int32), sr[:, :M].view(torch.int32))
+    assert torch.equal(s_col[:, :C].view(torch.int32), sc[:, :C].view(torch.int32))
+    rng = np.random.default_rng(16)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 30, replace=False)]))
+    q_o, s_o = quant.quant_rows(x[rows])
+    assert np.array_equal(host(q_row)[rows], q_o)
+    assert np.array_equal(scale_bits(host(s_row)[:, rows].T), scale_bits(s_o))
+    cols = np.unique(np.concatenate([[0, C - 1], rng.choice(C, 30, replace=False)]))
+    qc_o, sc_o = quant.quant_cols(x[:, cols])
+    assert np.array_equal(host(q_col)[cols], qc_o)
+    assert np.array_equal(scale_bits(host(s_col)[:, cols].T), scale_bits(sc_o))
+
+
 def assert_weight_match(fp8, w_bits, blocks=None, label=""):
     N, K = w_bits.shape
     q, s, q_t = fp8.quant_weight_128x128(dev(w_bits), transposed=True)

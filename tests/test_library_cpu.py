@@ -130,6 +130,31 @@ def test_gemm_validation(lib):
     assert gemm(lib, layout=2, N=200, ldc=208, ld_sb=200, dt=1) in (DEVICE, OK)
 
 
+def test_quant_dual_validation(lib):
+    f = lib.fp8_quant_act_dual
+    base = dict(x=X, rows=256, cols=384, ldx=384, qr=A, ldqr=384, sr=S, ldsr=256, qc=B, ldqc=256,
+                sc=S2, ldsc=384)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["x"], a["rows"], a["cols"], a["ldx"], a["qr"], a["ldqr"], a["sr"], a["ldsr"],
+                 a["qc"], a["ldqc"], a["sc"], a["ldsc"], None)
+    assert call(rows=200) == SHAPE
+    assert call(cols=200, ldx=208, ldqr=208, ldsc=208) == SHAPE
+    assert call(rows=0, x=None) == OK
+    assert call(qc=None) == NULL
+    assert call(sr=None) == NULL
+    assert call(ldx=256) == LD
+    assert call(ldqc=128) == LD
+    assert call(ldsr=128) == LD
+    assert call(ldsc=256) == LD
+    assert call(qr=A + 8) == ALIGN
+    assert call(ldqc=264) == ALIGN
+    assert call(qc=X) == ALIAS
+    assert call(qc=A) == ALIAS
+    assert call() in (DEVICE, OK)
+
+
 def test_grouped_validation(lib):
     f = lib.fp8_block_gemm_grouped
     args = [8, X, 1024, 256, 512, A, 512, S, 1024, B, 512, S2, C, 0, 256, None]

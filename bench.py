@@ -221,6 +221,9 @@ def main():
             # the same two quantizations as separate passes, for comparison
             tm.region("bwd.quant_row", lambda: fp8.quant_act_1x128(d["dy4"], "row"))
             tm.region("bwd.quant_col", lambda: fp8.quant_act_1x128(d["dy4"], "col"))
+            # X in both orientations from one read (Fprop rows, saved columns for Wgrad)
+            tm.region("fwd.quant_dual_x", lambda: fp8.quant_act_dual(d["x3"]))
+            tm.region("fwd.quant_row_x", lambda: fp8.quant_act_1x128(d["x3"], "row"))
         if want("grouped"):
             ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
             q, s, _ = tm.region("grouped.quant", lambda: fp8.quant_act_1x128(d["x5"], "row"))
@@ -321,6 +324,11 @@ def main():
                               "ms_separate_row_plus_col": trow + tcol,
                               "GB/s_separate": EL * 2 * (3 + 4 / 128) / (trow + tcol) / 1e6,
                               "speedup_vs_separate": (trow + tcol) / tdual}
+        tdx = tm.mean_ms("fwd.quant_dual_x")
+        tsx = tm.mean_ms("fwd.quant_row_x") + tm.mean_ms("wgrad.quant_x")
+        EX = 4096 * 7168
+        rows["dual_quant_x"] = {"ms": tdx, "GB/s": EX * (2 + 2 + 8 / 128) / tdx / 1e6,
+                                "ms_separate_row_plus_col": tsx, "speedup_vs_separate": tsx / tdx}
         # each GEMM is charged the share of the dual pass its operand costs
         tq1 = tq2 = tdual / 2
         rows["dgrad"] = {"ms_quant_share": tq1, "ms_gemm": tg1, "TFLOP/s_incl_quant": F3 / (tq1 + tg1) / 1e9,

@@ -22,6 +22,18 @@ __device__ __forceinline__ float scale_floor() { return __uint_as_float(kScaleFl
 
 // Max over the 16 lanes of a DPP row (one 1x128 tile = 16 lanes x 8 BF16);
 // every lane of the row ends with the row maximum.
+// Per-half max of two packed u16 values over each group of 8 consecutive lanes
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, a),
+                                                                __builtin_bit_cast(us2, b)));
+}
+__device__ __forceinline__ uint32_t row8_max_pk_u16(uint32_t t) {
+  t = pk_max_u16(t, (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+  t = pk_max_u16(t, (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+  t = pk_max_u16(t, (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  return t;
+}
+
 __device__ __forceinline__ uint32_t row16_max_u32(uint32_t t) {
   t = max(t, (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
   t = max(t, (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1

@@ -202,16 +202,18 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
 // MN-major scales) and the 128x1 column tiles (Wgrad operand, transposed
 // codes).  The row tiles are quantized from registers exactly as in
 // quant_rows_kernel (one 16-lane DPP row per tile row); the block is also
-// staged in LDS, where each thread takes two adjacent columns x 32 rows and
-// the column max is combined across the four row segments.  Every code and
-// scale equals the one the separate row and column quantizers produce.
+// staged in LDS, where eight lanes share two adjacent columns (16 rows each)
+// and combine the column max with DPP.  Input and codes are streamed
+// (non-temporal).  Every code and scale equals the one the separate row and
+// column quantizers produce.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_dual_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t ncb,
     uint8_t* __restrict__ q_row, int64_t ldq_row, float* __restrict__ s_row, int64_t ld_s_row,
     uint8_t* __restrict__ q_col, int64_t ldq_col, float* __restrict__ s_col, int64_t ld_s_col) {
-  __shared__ uint32_t tile[128][64];   // BF16 pairs: word c holds columns 2c, 2c+1
-  __shared__ uint32_t red[4][64];
+  // BF16 pairs: word c of row r holds columns 2c, 2c+1 and sits at word
+  // c ^ (8 * ((r >> 4) & 7)), so the column reads below hit 64 distinct banks
+  __shared__ uint32_t tile[128][64];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int sub = lane >> 4, l16 = lane & 15;
@@ -224,8 +226,9 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = wave * 32 + 4 * i + sub;
-    v[i] = *reinterpret_cast<const uint4*>(x + (r0 + row) * ldx + c0 + l16 * 8);
-    *reinterpret_cast<uint4*>(&tile[row][l16 * 4]) = v[i];
+    const sv4i u = __builtin_nontemporal_load(reinterpret_cast<const sv4i*>(x + (r0 + row) * ldx + c0 + l16 * 8));
+    v[i] = make_uint4((uint32_t)u.x, (uint32_t)u.y, (uint32_t)u.z, (uint32_t)u.w);
+    *reinterpret_cast<uint4*>(&tile[row][(l16 * 4) ^ (8 * ((row >> 4) & 7))]) = v[i];
   }
 
   // ---- 1x128 row tiles, from registers ----
@@ -246,52 +249,56 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
       out.x = pack4_sat_nan(bf16_lo(d.x) / s, bf16_hi(d.x) / s, bf16_lo(d.y) / s, bf16_hi(d.y) / s);
       out.y = pack4_sat_nan(bf16_lo(d.z) / s, bf16_hi(d.z) / s, bf16_lo(d.w) / s, bf16_hi(d.w) / s);
     }
-    *reinterpret_cast<uint2*>(q_row + (r0 + row) * ldq_row + c0 + l16 * 8) = out;
+    __builtin_nontemporal_store(sv2i{(int)out.x, (int)out.y},
+                                reinterpret_cast<sv2i*>(q_row + (r0 + row) * ldq_row + c0 + l16 * 8));
     if (l16 == 0) s_row[kb * ld_s_row + r0 + row] = s;
   }
   __syncthreads();
 
-  // ---- 128x1 column tiles, from LDS: columns 2p, 2p+1, rows seg*32.. ----
-  const int p = t & 63, seg = t >> 6;
-  uint32_t d[32];
-  us2 m = {0, 0};
+  // ---- 128x1 column tiles, from LDS ----
+  // Lane 8j + g of wave w takes column pair cp = 32*pass + 8w + j and rows
+  // 16g..16g+15; the 8 lanes of a pair reduce its amax with DPP and then
+  // write each column's 128 codes as one contiguous 128-byte run.
+  const int g = lane & 7, j = lane >> 3;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    d[i] = tile[seg * 32 + i][p];
-    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[i] & 0x7FFF7FFFu));
-  }
-  red[seg][p] = __builtin_bit_cast(uint32_t, m);
-  __syncthreads();
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cp = 32 * pass + 8 * wave + j;
+    uint32_t d[16];
+    us2 m = {0, 0};
 #pragma unroll
-  for (int g = 0; g < 4; ++g) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, red[g][p]));
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t tt = h ? m.y : m.x;
-    const float s = tile_scale(tt);
-    uint32_t w[8];
-    if (tt < kBf16InfAbs) {
-      const float r = 1.0f / s;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = div_by_scale(h ? bf16_hi(d[4 * k + e]) : bf16_lo(d[4 * k + e]), s, r);
-        w[k] = pack4_sat(y[0], y[1], y[2], y[3]);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (h ? bf16_hi(d[4 * k + e]) : bf16_lo(d[4 * k + e])) / s;
-        w[k] = pack4_sat_nan(y[0], y[1], y[2], y[3]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      d[i] = tile[16 * g + i][cp ^ (8 * g)];
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[i] & 0x7FFF7FFFu));
     }
-    const int64_t col = c0 + 2 * p + h;
-    uint4* dst = reinterpret_cast<uint4*>(q_col + col * ldq_col + r0 + seg * 32);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    if (seg == 0) s_col[rb * ld_s_col + col] = s;
+    const uint32_t mm = row8_max_pk_u16(__builtin_bit_cast(uint32_t, m));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t tt = h ? (mm >> 16) : (mm & 0xFFFFu);
+      const float s = tile_scale(tt);
+      uint32_t w[4];
+      if (tt < kBf16InfAbs) {
+        const float r = 1.0f / s;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = div_by_scale(h ? bf16_hi(d[4 * k + e]) : bf16_lo(d[4 * k + e]), s, r);
+          w[k] = pack4_sat(y[0], y[1], y[2], y[3]);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = (h ? bf16_hi(d[4 * k + e]) : bf16_lo(d[4 * k + e])) / s;
+          w[k] = pack4_sat_nan(y[0], y[1], y[2], y[3]);
+        }
+      }
+      const int64_t col = c0 + 2 * cp + h;
+      __builtin_nontemporal_store(sv4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
+                                  reinterpret_cast<sv4i*>(q_col + col * ldq_col + r0 + 16 * g));
+      if (g == 0) s_col[rb * ld_s_col + col] = s;
+    }
   }
 }
 

@@ -116,17 +116,24 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 
 // ---------------------------------------------------------------------------
 // 128x1 column tiles, transposed output.  A workgroup stages a 128-row x
-// 64-column BF16 block in LDS (coalesced 16-byte row loads), each thread
-// takes two adjacent columns x 16 rows, the column max is combined across the
-// eight row segments through LDS, and every column's 128 codes are written as
-// contiguous 16-byte pieces of the transposed output row.
+// 64-column BF16 block in LDS (coalesced 16-byte row loads).  Lane 8j + g of
+// wave w then takes the column pair 8w + j over rows 16g..16g+15; the eight
+// lanes of a pair combine the column max with DPP, and each writes 16 codes,
+// so every store instruction covers whole 128-byte runs of eight transposed
+// output rows.  LDS layout: 16-row group g starts at word 544*g (32 words of
+// padding after every group) and its rows are rotated by 8*(g >> 1) words,
+// which puts the 64 lanes of a column read on 64 distinct banks.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int cols_tile_word(int row, int word) {
+  const int g = row >> 4;
+  return g * 544 + (row & 15) * 32 + ((word + 8 * (g >> 1)) & 31);
+}
+
 __global__ __launch_bounds__(256) void quant_cols_kernel(
     const uint16_t* __restrict__ x, int64_t cols, int64_t ldx, int64_t ncb,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int64_t ld_s,
     float* __restrict__ amax_out) {
-  __shared__ uint32_t tile[128][32];
-  __shared__ uint32_t red[8][32];
+  __shared__ uint32_t tile[8 * 544];
   const int t = threadIdx.x;
   const int64_t rb = blockIdx.x / ncb;
   const int64_t c0 = (blockIdx.x % ncb) * 64;
@@ -145,25 +152,22 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
       for (int e = 0; e < 8 && col + e < cols; ++e) h[e] = src[e];
       val = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
     }
-    *reinterpret_cast<uint4*>(&tile[row][cc * 4]) = val;
+    *reinterpret_cast<uint4*>(&tile[cols_tile_word(row, cc * 4)]) = val;
   }
   __syncthreads();
-  const int p = t & 31, seg = t >> 5;
+  const int lane = t & 63, g = lane & 7;
+  const int p = 8 * (t >> 6) + (lane >> 3);
   uint32_t d[16];
   us2 m = {0, 0};
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    d[i] = tile[seg * 16 + i][p];
+    d[i] = tile[cols_tile_word(16 * g + i, p)];
     m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[i] & 0x7FFF7FFFu));
   }
-  red[seg][p] = __builtin_bit_cast(uint32_t, m);
-  __syncthreads();
-#pragma unroll
-  for (int s = 0; s < 8; ++s) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, red[s][p]));
-  const uint32_t ta = m.x, tb = m.y;
+  const uint32_t mm = row8_max_pk_u16(__builtin_bit_cast(uint32_t, m));
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t tt = h ? tb : ta;
+    const uint32_t tt = h ? (mm >> 16) : (mm & 0xFFFFu);
     const float s = tile_scale(tt);
     float y[16];
 #pragma unroll
@@ -187,8 +191,8 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
     }
     const int64_t col = c0 + 2 * p + h;
     if (col < cols) {
-      *reinterpret_cast<uint4*>(q + col * ldq + r0 + seg * 16) = out;
-      if (seg == 0) {
+      *reinterpret_cast<uint4*>(q + col * ldq + r0 + 16 * g) = out;
+      if (g == 0) {
         scales[rb * ld_s + col] = s;
         if (amax_out) amax_out[rb * ld_s + col] = amax_value(tt);
       }

@@ -2,7 +2,8 @@
 
 This module produces the input tensors only: Gaussian activations with
 channel-concentrated outliers, Gaussian weights and gradients, the drifting
-tile sequence of the online-scaling worked example, and expert token counts.
+tile sequence of the online-scaling worked example, expert token counts and
+the dispatch order of routed token copies.
 It holds none of the quantization or GEMM arithmetic; the oracle and the HIP
 path both consume what it returns.
 
@@ -18,6 +19,7 @@ from .generators import (  # noqa: F401
     drift_sequence,
     expert_counts,
     expert_offsets,
+    dispatch_rows,
     lossless_tiles,
     CONFIGS,
 )

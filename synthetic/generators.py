@@ -119,6 +119,21 @@ def expert_offsets(counts) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
 
 
+def dispatch_rows(tokens: int, experts: int, topk: int, seed: int = 0) -> np.ndarray:
+    """Source token of every dispatched copy, grouped by expert.
+
+    Each token picks ``topk`` distinct experts uniformly at random (seeded);
+    the copies are listed expert by expert, tokens ascending within an expert.
+    Returns int32 [tokens * topk].
+    """
+    rng = np.random.default_rng(seed)
+    choice = np.argsort(rng.random((tokens, experts)), axis=1)[:, :topk]   # distinct experts
+    tok = np.repeat(np.arange(tokens), topk)
+    exp = choice.reshape(-1)
+    order = np.lexsort((tok, exp))
+    return tok[order].astype(np.int32)
+
+
 def lossless_tiles(rows: int, cols: int, seed: int, tile=(1, 128), k_range=(-30, 20)):
     """BF16 bits whose every scaling tile is exactly representable.
 

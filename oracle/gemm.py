@@ -131,8 +131,8 @@ def round_to_bf16_bits(r) -> np.ndarray:
     q = np.rint(np.ldexp(rr, -spacing_exp))             # exact scaling, then RNE
     v = np.ldexp(q, spacing_exp)
     v = np.where(np.abs(v) >= 2.0 ** 128, np.copysign(np.inf, rr), v)
+    v = np.where(r == 0.0, np.copysign(0.0, r), v)
     v = np.where(inf, r, v)
-    v = np.where(rr == 0.0, np.copysign(0.0, r), v)
     bits = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     return np.where(nan, np.uint16(0x7FC0), bits).astype(np.uint16)
 

@@ -147,6 +147,16 @@ def test_round_to_bf16_no_double_rounding():
     assert gemm.round_to_bf16_bits(np.array([np.nan]))[0] == 0x7FC0
 
 
+def test_round_to_bf16_special_values_match_torch():
+    # torch's CPU float32 -> bfloat16 cast (round to nearest even) on values
+    # where one rounding from float64 and one from float32 agree
+    import torch
+    v = np.array([np.inf, -np.inf, 0.0, -0.0, 1.0, -3.0, 2.0 ** -133, -(2.0 ** -126),
+                  3.3895e38, -3.3895e38, 3.4e38, 65504.0, 1e-40], np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(gemm.round_to_bf16_bits(v.astype(np.float64)), want)
+
+
 def test_ulp_bf16():
     assert gemm.ulp_bf16(np.array([1.0]))[0] == 2.0 ** -7
     assert gemm.ulp_bf16(np.array([1.99]))[0] == 2.0 ** -7

@@ -14,6 +14,9 @@ seeded synthetic inputs already resident in HBM:
              passes ("dual_quant")
   grouped    1x128 quantization of X 16384x7168 + one grouped launch over 8
              experts (multinomial token counts), W_e 2048x7168
+  payload    FP8 token messages for the dispatch of X 4096x7168 to top-2 of
+             8 experts (8192 messages of 7392 bytes, gathered in expert
+             order): pack, unpack into the GEMM operand layout, restore BF16
   weights    128x128 quantization of W 18432x7168 with the transposed copy
   policy     one caller-scale (history policy) quantization of a 128x7168 tile
              with amax and saturation count, plus the history update
@@ -167,10 +170,14 @@ def main():
     if want("fprop") or want("backward") or want("weights"):
         host["w3"] = syn.gaussian((18432, 7168), seed=1, std=0.02)
         d["w3"] = to_dev(host["w3"], torch)
-    if want("fprop") or want("backward"):
+    if want("fprop") or want("backward") or want("payload"):
         host["x3"] = syn.activation_with_outliers(4096, 7168, seed=0)
         d["x3"] = to_dev(host["x3"], torch)
+    if want("fprop") or want("backward"):
         d["wq3"], d["ws3"], d["wq3t"] = fp8.quant_weight_128x128(d["w3"], transposed=True)  # untimed
+    if want("payload"):
+        d["src6"] = to_dev(syn.dispatch_rows(4096, 8, 2, seed=5), torch)
+        d["msg6"] = fp8.pack_tokens(d["x3"], d["src6"])
     if want("backward"):
         d["dy4"] = to_dev(syn.gaussian((4096, 18432), seed=4, std=1e-3), torch)
     if want("grouped"):
@@ -230,6 +237,10 @@ def main():
             tm.region("grouped.gemm", lambda: fp8.block_gemm_grouped(d["off5"], q, s, d["wq5"], d["ws5"]))
             ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
             tm.pending.append(("grouped", ev0, ev1))
+        if want("payload"):
+            tm.region("payload.pack", lambda: fp8.pack_tokens(d["x3"], d["src6"], out=d["msg6"]))
+            tm.region("payload.unpack", lambda: fp8.unpack_tokens(d["msg6"], 7168))
+            tm.region("payload.dequant", lambda: fp8.dequant_tokens(d["msg6"], 7168))
         if want("weights"):
             tm.region("weights", lambda: fp8.quant_weight_128x128(d["w3"], transposed=True))
         if want("policy"):
@@ -347,6 +358,13 @@ def main():
         B = 18432 * 7168 * 4 + (18432 // 128) * (7168 // 128) * 4
         t = tm.mean_ms("weights")
         rows["weights"] = {"ms": t, "GB/s": B / t / 1e6}
+    if want("payload"):
+        n_msg, MB = 8192, 7392
+        tp, tu, tdq = tm.mean_ms("payload.pack"), tm.mean_ms("payload.unpack"), tm.mean_ms("payload.dequant")
+        rows["payload"] = {"messages": n_msg, "message_bytes": MB,
+                           "ms_pack": tp, "GB/s_pack": n_msg * (2 * 7168 + MB) / tp / 1e6,
+                           "ms_unpack": tu, "GB/s_unpack": n_msg * 2 * MB / tu / 1e6,
+                           "ms_dequant": tdq, "GB/s_dequant": n_msg * (MB + 2 * 7168) / tdq / 1e6}
     if want("policy"):
         rows["policy"] = {"ms": tm.mean_ms("policy")}
     if want("copy"):

@@ -153,6 +153,59 @@ fp8_status fp8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
+fp8_status fp8_pack_tokens(const void* x, int64_t x_rows, int64_t H, int64_t ldx,
+                           const int32_t* src_rows, int64_t T, uint8_t* msg, int64_t stride,
+                           void* stream) {
+  if (x_rows < 0 || H < 0 || T < 0 || H % 128 != 0) return FP8_ERR_SHAPE;
+  if (!src_rows && T > x_rows) return FP8_ERR_SHAPE;
+  if (T == 0 || H == 0) return FP8_OK;
+  if (!msg || (!x && x_rows > 0)) return FP8_ERR_NULL;
+  if (ldx < H || stride < H + H / 32) return FP8_ERR_LD;
+  if (!aligned16(x) || !aligned16(msg) || (ldx * 2) % 16 != 0 || stride % 16 != 0 ||
+      !aligned4(src_rows))
+    return FP8_ERR_ALIGN;
+  const Range rm = span(msg, T, H + H / 32, stride);
+  if (overlap(rm, span(x, x_rows, H * 2, ldx * 2))) return FP8_ERR_ALIAS;
+  if (src_rows && overlap(rm, span(src_rows, 1, T * 4, T * 4))) return FP8_ERR_ALIAS;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  return launched(fp8bs::launch_pack_tokens(static_cast<const uint16_t*>(x), x_rows, H, ldx, src_rows,
+                                            T, msg, stride, reinterpret_cast<hipStream_t>(stream)));
+}
+
+fp8_status fp8_unpack_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t stride, uint8_t* q,
+                             int64_t ldq, float* scales, int64_t ld_s, void* stream) {
+  if (T < 0 || H < 0 || H % 128 != 0) return FP8_ERR_SHAPE;
+  if (T == 0 || H == 0) return FP8_OK;
+  if (!msg || !q || !scales) return FP8_ERR_NULL;
+  if (stride < H + H / 32 || ldq < H || ld_s < T) return FP8_ERR_LD;
+  if (!aligned16(msg) || !aligned16(q) || stride % 16 != 0 || ldq % 16 != 0 || !aligned4(scales))
+    return FP8_ERR_ALIGN;
+  const Range rm = span(msg, T, H + H / 32, stride);
+  const Range rq = span(q, T, H, ldq);
+  const Range rs = span(scales, H / 128, T * 4, ld_s * 4);
+  if (overlap(rq, rm) || overlap(rs, rm) || overlap(rq, rs)) return FP8_ERR_ALIAS;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  return launched(fp8bs::launch_unpack_tokens(msg, T, H, stride, q, ldq, scales, ld_s,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+fp8_status fp8_dequant_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t stride, void* y,
+                              int64_t ldy, void* stream) {
+  if (T < 0 || H < 0 || H % 128 != 0) return FP8_ERR_SHAPE;
+  if (T == 0 || H == 0) return FP8_OK;
+  if (!msg || !y) return FP8_ERR_NULL;
+  if (stride < H + H / 32 || ldy < H) return FP8_ERR_LD;
+  if (!aligned16(msg) || !aligned16(y) || stride % 16 != 0 || (ldy * 2) % 16 != 0)
+    return FP8_ERR_ALIGN;
+  if (overlap(span(y, T, H * 2, ldy * 2), span(msg, T, H + H / 32, stride))) return FP8_ERR_ALIAS;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  return launched(fp8bs::launch_dequant_tokens(msg, T, H, stride, static_cast<uint16_t*>(y), ldy,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
 fp8_status fp8_quant_weight_128x128(const void* w, int64_t rows, int64_t cols, int64_t ldw,
                                     uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
                                     float* scales, int64_t ld_s, void* stream) {

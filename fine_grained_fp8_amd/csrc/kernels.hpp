@@ -31,6 +31,17 @@ hipError_t launch_history_update(float* hist, const float* amax, int64_t n, floa
 
 hipError_t launch_cast_e4m3(const float* x, int64_t n, uint8_t* q, hipStream_t stream);
 
+hipError_t launch_pack_tokens(const uint16_t* x, int64_t x_rows, int64_t H, int64_t ldx,
+                              const int32_t* src_rows, int64_t T, uint8_t* msg, int64_t stride,
+                              hipStream_t stream);
+
+hipError_t launch_unpack_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t stride,
+                                uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                                hipStream_t stream);
+
+hipError_t launch_dequant_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t stride,
+                                 uint16_t* y, int64_t ldy, hipStream_t stream);
+
 enum GemmLayout { kFprop = 0, kDgrad = 1, kWgrad = 2, kDgradT = 3 };
 
 struct GemmProblem {

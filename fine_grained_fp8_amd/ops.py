@@ -204,3 +204,58 @@ def cast_e4m3(x: torch.Tensor, *, out=None, stream=None):
     st = lib.fp8_cast_e4m3(_ptr(x), x.numel(), _ptr(out), _stream(stream))
     _lib.check("fp8_cast_e4m3", st)
     return out
+
+
+def message_bytes(H: int) -> int:
+    """Bytes of one token message: H codes + H/128 FP32 scales."""
+    return H + H // 32
+
+
+def pack_tokens(x: torch.Tensor, src_rows=None, *, T=None, stride=None, out=None, stream=None):
+    """Quantize tokens x [rows][H] BF16 into messages uint8 [T][stride].
+
+    src_rows: optional int32 device tensor [T]; message t carries row
+    src_rows[t] (dispatch order).  Default: every row in order.
+    stride defaults to round_up(H + H/32, 16).
+    """
+    lib = _lib.load_library()
+    _check_2d("x", x, _BF16)
+    rows, H = x.shape
+    if src_rows is not None:
+        if src_rows.dtype != torch.int32 or src_rows.dim() != 1 or not src_rows.is_contiguous():
+            raise ValueError("src_rows: contiguous 1-D int32 device tensor required")
+        T = src_rows.numel()
+    elif T is None:
+        T = rows
+    stride = round_up(message_bytes(H), 16) if stride is None else stride
+    if out is None:
+        out = torch.empty((T, stride), dtype=torch.uint8, device=x.device)
+    st = lib.fp8_pack_tokens(_ptr(x), rows, H, x.stride(0), _ptr(src_rows), T, _ptr(out),
+                             out.stride(0), _stream(stream))
+    _lib.check("fp8_pack_tokens", st)
+    return out
+
+
+def unpack_tokens(msg: torch.Tensor, H: int, *, stream=None):
+    """Messages [T][stride] -> (q [T][H] uint8, scales [H/128][round_up(T, 4)] float32),
+    the operand layout of quant_act_1x128(..., "row")."""
+    lib = _lib.load_library()
+    _check_2d("msg", msg, (torch.uint8,))
+    T = msg.shape[0]
+    q = torch.empty((T, H), dtype=torch.uint8, device=msg.device)
+    s = torch.empty((H // 128, round_up(T, 4)), dtype=torch.float32, device=msg.device)
+    st = lib.fp8_unpack_tokens(_ptr(msg), T, H, msg.stride(0), _ptr(q), q.stride(0), _ptr(s),
+                               s.stride(0), _stream(stream))
+    _lib.check("fp8_unpack_tokens", st)
+    return q, s
+
+
+def dequant_tokens(msg: torch.Tensor, H: int, *, stream=None):
+    """Messages [T][stride] -> BF16 [T][H]: decode(q) * s rounded once to BF16."""
+    lib = _lib.load_library()
+    _check_2d("msg", msg, (torch.uint8,))
+    T = msg.shape[0]
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=msg.device)
+    st = lib.fp8_dequant_tokens(_ptr(msg), T, H, msg.stride(0), _ptr(y), y.stride(0), _stream(stream))
+    _lib.check("fp8_dequant_tokens", st)
+    return y

@@ -229,6 +229,53 @@ fp8_status fp8_amax_history_update(float* hist, const float* amax, int64_t n, fl
  */
 fp8_status fp8_cast_e4m3(const float* x, int64_t n, uint8_t* q, void* stream);
 
+/*
+ * FP8 token payloads - one self-contained message per token for activations
+ * kept for the backward pass and for the tokens sent to experts in the MoE
+ * all-to-all ("FP8 Mixed Precision: DeepSeek-V3 Training Architecture",
+ * section 4: cached activations and dispatched tokens in FP8, and its section
+ * on the MoE all-to-all: each dispatched token is one hidden vector).
+ *
+ * Message layout for H channels (H % 128 == 0), H + H/32 bytes:
+ *   bytes [0, H)           E4M3 codes of the token's 1x128 tiles (the online
+ *                          rule above, identical to fp8_quant_act_1x128 ROW)
+ *   bytes [H, H + H/32)    the H/128 FP32 tile scales, little-endian, in tile order
+ * Messages sit at `stride` bytes (stride >= H + H/32, stride % 16 == 0);
+ * bytes past a message are not written.  7168 channels: 7392 bytes, 33/64 of
+ * the BF16 row.
+ */
+
+/*
+ * fp8_pack_tokens - quantize tokens into messages.
+ *  x         BF16 [x_rows][ldx >= H]
+ *  src_rows  optional int32 [T] device array: message t carries row
+ *            src_rows[t] (the dispatch order; rows may repeat).  NULL: row t
+ *            (then T <= x_rows).  A src_rows entry outside [0, x_rows) gives a
+ *            message of NaN codes (0x7F) and NaN scales (0x7FC00000).
+ *  msg       [T][stride] bytes; must not overlap x or src_rows.
+ */
+fp8_status fp8_pack_tokens(const void* x, int64_t x_rows, int64_t H, int64_t ldx,
+                           const int32_t* src_rows, int64_t T, uint8_t* msg, int64_t stride,
+                           void* stream);
+
+/*
+ * fp8_unpack_tokens - messages into the GEMM operand layout of
+ * fp8_quant_act_1x128 ROW: codes q [T][ldq >= H] and MN-major scales
+ * [H/128][ld_s >= T] (byte copies: bit-exact).  Outputs must not overlap msg
+ * or each other.
+ */
+fp8_status fp8_unpack_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t stride, uint8_t* q,
+                             int64_t ldq, float* scales, int64_t ld_s, void* stream);
+
+/*
+ * fp8_dequant_tokens - restore BF16 from messages: y [T][ldy >= H] with
+ * y = decode(q) * s rounded once to BF16 (nearest, ties to even) from the
+ * exact product; NaN codes or scales give 0x7FC0, 0 * Inf gives 0x7FC0.
+ * y must not overlap msg.
+ */
+fp8_status fp8_dequant_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t stride, void* y,
+                              int64_t ldy, void* stream);
+
 /* Static string naming a status; never NULL. */
 const char* fp8_status_string(fp8_status s);
 

@@ -155,6 +155,50 @@ def test_quant_dual_validation(lib):
     assert call() in (DEVICE, OK)
 
 
+def test_payload_validation(lib):
+    # H = 256: message 264 bytes, stride 272
+    pack = lambda x=X, rows=64, H=256, ldx=256, src=None, T=64, msg=Q, stride=272: \
+        lib.fp8_pack_tokens(x, rows, H, ldx, src, T, msg, stride, None)
+    assert pack(H=200, ldx=200) == SHAPE
+    assert pack(T=65) == SHAPE                   # no src_rows: T <= rows
+    assert pack(T=-1) == SHAPE
+    assert pack(T=0, msg=None) == OK
+    assert pack(msg=None) == NULL
+    assert pack(x=None) == NULL
+    assert pack(ldx=128) == LD
+    assert pack(stride=256) == LD                # < 264
+    assert pack(stride=264) == ALIGN             # not a multiple of 16
+    assert pack(x=X + 8) == ALIGN
+    assert pack(src=A + 2, T=100) == ALIGN
+    assert pack(msg=X) == ALIAS
+    assert pack(src=Q + 64, T=100) == ALIAS      # src_rows inside the messages
+    assert pack(src=A, T=100) in (DEVICE, OK)    # gathering: T may exceed rows
+    assert pack() in (DEVICE, OK)
+
+    unpack = lambda msg=Q, T=64, H=256, stride=272, q=A, ldq=256, s=S, lds=64: \
+        lib.fp8_unpack_tokens(msg, T, H, stride, q, ldq, s, lds, None)
+    assert unpack(H=100) == SHAPE
+    assert unpack(q=None) == NULL
+    assert unpack(lds=60) == LD
+    assert unpack(ldq=128) == LD
+    assert unpack(stride=200) == LD
+    assert unpack(ldq=264) == ALIGN
+    assert unpack(s=S + 2) == ALIGN
+    assert unpack(q=Q + 16) == ALIAS
+    assert unpack(s=A + 64) == ALIAS
+    assert unpack() in (DEVICE, OK)
+
+    deq = lambda msg=Q, T=64, H=256, stride=272, y=A, ldy=256: \
+        lib.fp8_dequant_tokens(msg, T, H, stride, y, ldy, None)
+    assert deq(H=-128) == SHAPE
+    assert deq(y=None) == NULL
+    assert deq(ldy=128) == LD
+    assert deq(ldy=260) == ALIGN
+    assert deq(y=Q + 256) == ALIAS
+    assert deq(T=0, y=None) == OK
+    assert deq() in (DEVICE, OK)
+
+
 def test_grouped_validation(lib):
     f = lib.fp8_block_gemm_grouped
     args = [8, X, 1024, 256, 512, A, 512, S, 1024, B, 512, S2, C, 0, 256, None]

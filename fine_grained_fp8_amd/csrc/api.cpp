@@ -206,6 +206,25 @@ fp8_status fp8_dequant_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t 
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
+fp8_status fp8_gemm_promotion(const uint8_t* A, int64_t M, int64_t K, int64_t lda, const uint8_t* B,
+                              int64_t N, int64_t ldb, int64_t promote_k, float* C, int64_t ldc,
+                              void* stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8_ERR_SHAPE;
+  if (!(promote_k == 32 || promote_k == 64 || (promote_k >= 128 && promote_k % 128 == 0)))
+    return FP8_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return FP8_OK;
+  if (!C || (K > 0 && (!A || !B))) return FP8_ERR_NULL;
+  if (lda < K || ldb < K || ldc < N) return FP8_ERR_LD;
+  if (!aligned16(A) || !aligned16(B) || lda % 16 != 0 || ldb % 16 != 0 || !aligned4(C))
+    return FP8_ERR_ALIGN;
+  const Range rc = span(C, M, N * 4, ldc * 4);
+  if (overlap(rc, span(A, M, K, lda)) || overlap(rc, span(B, N, K, ldb))) return FP8_ERR_ALIAS;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  return launched(fp8bs::launch_gemm_promotion(A, lda, B, ldb, M, N, K, promote_k, C, ldc,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
 fp8_status fp8_quant_weight_128x128(const void* w, int64_t rows, int64_t cols, int64_t ldw,
                                     uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
                                     float* scales, int64_t ld_s, void* stream) {

@@ -42,6 +42,10 @@ hipError_t launch_unpack_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_
 hipError_t launch_dequant_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t stride,
                                  uint16_t* y, int64_t ldy, hipStream_t stream);
 
+hipError_t launch_gemm_promotion(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                                 int64_t M, int64_t N, int64_t K, int64_t promote_k, float* C,
+                                 int64_t ldc, hipStream_t stream);
+
 enum GemmLayout { kFprop = 0, kDgrad = 1, kWgrad = 2, kDgradT = 3 };
 
 struct GemmProblem {

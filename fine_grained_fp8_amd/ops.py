@@ -259,3 +259,21 @@ def dequant_tokens(msg: torch.Tensor, H: int, *, stream=None):
     st = lib.fp8_dequant_tokens(_ptr(msg), T, H, msg.stride(0), _ptr(y), y.stride(0), _stream(stream))
     _lib.check("fp8_dequant_tokens", st)
     return y
+
+
+def gemm_promotion(A: torch.Tensor, B: torch.Tensor, promote_k: int, *, stream=None):
+    """C [M][N] FP32 = A [M][K] . B [N][K]^T over E4M3 codes (unit scales), with
+    the matrix unit's accumulator promoted to FP32 every promote_k values of K
+    (32, 64 or a multiple of 128; >= K: one accumulator chain)."""
+    lib = _lib.load_library()
+    _check_2d("A", A, (torch.uint8,))
+    _check_2d("B", B, (torch.uint8,))
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError(f"A {tuple(A.shape)} and B {tuple(B.shape)}: K differs")
+    C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    st = lib.fp8_gemm_promotion(_ptr(A), M, K, A.stride(0), _ptr(B), N, B.stride(0), promote_k,
+                                _ptr(C), C.stride(0), _stream(stream))
+    _lib.check("fp8_gemm_promotion", st)
+    return C

@@ -230,6 +230,29 @@ fp8_status fp8_amax_history_update(float* hist, const float* amax, int64_t n, fl
 fp8_status fp8_cast_e4m3(const float* x, int64_t n, uint8_t* q, void* stream);
 
 /*
+ * fp8_gemm_promotion - accumulation-precision study: C = A . B^T over E4M3
+ * codes with unit scales, FP32 out, with a chosen promotion interval
+ * ("Introduction to LLM Quantization", section 3: tensor cores keep FP8 sums
+ * with limited precision, so partial sums are promoted to FP32 at a fixed
+ * interval; "FP8 Mixed Precision: DeepSeek-V3 Training Architecture",
+ * section 3).
+ *  A  [M][lda >= K] codes, B [N][ldb >= K] codes (both K-contiguous);
+ *     K % 128 == 0, lda % 16 == 0, ldb % 16 == 0.
+ *  promote_k  a multiple of 128: the matrix unit's accumulator is carried
+ *             over promote_k / 128 consecutive 128-wide K blocks, then added
+ *             to an FP32 running sum (128 = the method, bit-identical to
+ *             fp8_block_gemm FPROP with unit scales and FP32 output;
+ *             >= K = a single accumulator chain).  32 or 64: each 128-wide
+ *             block's partial is formed per 32- or 64-wide sub-block and each
+ *             is added to the running sum.  Other values: FP8_ERR_UNSUPPORTED.
+ *  C  FP32 [M][ldc >= N]; must not overlap A or B.
+ *  A reference kernel (one wave per 16x16 tile), not tuned for speed.
+ */
+fp8_status fp8_gemm_promotion(const uint8_t* A, int64_t M, int64_t K, int64_t lda, const uint8_t* B,
+                              int64_t N, int64_t ldb, int64_t promote_k, float* C, int64_t ldc,
+                              void* stream);
+
+/*
  * FP8 token payloads - one self-contained message per token for activations
  * kept for the backward pass and for the tokens sent to experts in the MoE
  * all-to-all ("FP8 Mixed Precision: DeepSeek-V3 Training Architecture",

@@ -199,6 +199,25 @@ def test_payload_validation(lib):
     assert deq() in (DEVICE, OK)
 
 
+def test_gemm_promotion_validation(lib):
+    f = lambda A_=A, M=64, K=256, lda=256, B_=B, N=48, ldb=256, pk=128, C_=C, ldc=48: \
+        lib.fp8_gemm_promotion(A_, M, K, lda, B_, N, ldb, pk, C_, ldc, None)
+    assert f(K=200, lda=208, ldb=208) == SHAPE
+    assert f(M=-1) == SHAPE
+    for pk in (0, 16, 96, 200, -128):
+        assert f(pk=pk) == UNSUP
+    assert f(M=0, C_=None) == OK
+    assert f(C_=None) == NULL
+    assert f(A_=None) == NULL
+    assert f(lda=128) == LD
+    assert f(ldc=32) == LD
+    assert f(lda=264) == ALIGN
+    assert f(A_=A + 4) == ALIGN
+    assert f(C_=A + 1024) == ALIAS
+    for pk in (32, 64, 128, 384, 1 << 20):
+        assert f(pk=pk) in (DEVICE, OK)
+
+
 def test_grouped_validation(lib):
     f = lib.fp8_block_gemm_grouped
     args = [8, X, 1024, 256, 512, A, 512, S, 1024, B, 512, S2, C, 0, 256, None]

@@ -78,3 +78,16 @@ def test_relative_errors_closed_form():
     e = acc.relative_errors(C, R, T=np.full((2, 2), 10.0))
     assert np.isclose(e["norm"], np.sqrt(0.25 + 1.0) / np.sqrt(21.0))
     assert e["median_rel"] == 0.0 and np.isclose(e["max_over_T"], 0.1)
+
+
+def test_fourteen_bit_picture_matches_the_pages_figure():
+    # "Introduction to LLM Quantization" section 3: with about 14 bits of
+    # accumulation, K = 4096 gives relative errors of up to about 2%.  The
+    # running-sum model at 14 bits (nearest-even) on Gaussian FP8 products:
+    # the tail of the per-element relative error sits at that figure.
+    A, B = _codes((32, 4096), 11), _codes((32, 4096), 12)
+    e = acc.relative_errors(acc.running_sum(A, B, 14, "rne"), acc.exact(A, B))
+    assert 0.005 < e["p99_rel"] < 0.1
+    assert e["norm"] < 0.005                 # the bulk stays well below it
+    e24 = acc.relative_errors(acc.running_sum(A, B, 24, "rne"), acc.exact(A, B))
+    assert e24["p99_rel"] < 1e-4             # FP32 accumulation: no such tail

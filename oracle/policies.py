@@ -11,6 +11,8 @@ Sources:
   mean error).
 * "Introduction to LLM Quantization", section 5: delayed quantization derives
   the current scale from past maxima and can overflow when the range moves.
+* "Online Quantization During Training", study lab: saturation through a
+  curriculum change (``synthetic.curriculum_sequence``).
 
 Policies, per 1x128 tile (readings where the pages are silent):
 
@@ -20,6 +22,8 @@ Policies, per 1x128 tile (readings where the pages are silent):
   (FP32, no fused multiply-add).  Step t >= 1 quantizes with
   s_t = max(fl32(h_{t-1} / 448), fl32(1e-12)), so step 0 equals ``current``.
 * ``fixed``: the step-0 online scales, reused for every step.
+* ``clip<r>`` (e.g. ``clip2``): percentile clipping of the current tile, the
+  clip value being its r-th largest |x| (``oracle.granularity``).
 
 Per step the oracle records the saturation count (elements whose rounded
 scaled value lies beyond 448 before the clip, i.e. |fl32(x / s)| > 464), the
@@ -31,7 +35,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import e4m3, quant
+from . import e4m3, granularity, quant
 
 DECAY = np.float32(0.9)
 
@@ -75,6 +79,8 @@ def simulate(sequence, policies=("current", "history", "fixed")):
                 s = s_cur if hist is None else quant.scale_from_amax(hist)
             elif p == "fixed":
                 s = s_cur if fixed is None else fixed
+            elif p.startswith("clip"):
+                s = granularity.tile_scales(x_bits, 128, int(p[4:]))
             else:
                 raise ValueError(p)
             q, _, sat = quant.quant_rows_external(x_bits, s)

@@ -3,7 +3,8 @@
 This module produces the input tensors only: Gaussian activations with
 channel-concentrated outliers, Gaussian weights and gradients, the drifting
 tile sequence of the online-scaling worked example, expert token counts and
-the dispatch order of routed token copies.
+the dispatch order of routed token copies, and a tile sequence whose
+distribution jumps (a curriculum change).
 It holds none of the quantization or GEMM arithmetic; the oracle and the HIP
 path both consume what it returns.
 
@@ -17,6 +18,7 @@ from .generators import (  # noqa: F401
     gaussian,
     toy_layer,
     drift_sequence,
+    curriculum_sequence,
     expert_counts,
     expert_offsets,
     dispatch_rows,

@@ -108,6 +108,24 @@ def drift_sequence(steps: int = 100, M: int = 128, K: int = 7168, seed: int = 0,
         yield t, sigma, f32_to_bf16_bits(x)
 
 
+def curriculum_sequence(steps: int = 100, M: int = 128, K: int = 7168, seed: int = 0,
+                        shifts=((40, 4.0), (70, 1.0))):
+    """Yield (t, sigma_t, X_t bits) for a data mix that changes abruptly.
+
+    sigma_t = 1 until the first shift step, then the factor of the latest
+    shift reached (default: 4x from step 40, back to 1x from step 70);
+    X_t = sigma_t N(0, 1), a fresh seeded draw per step.
+    """
+    for t in range(steps):
+        sigma = 1.0
+        for step, factor in shifts:
+            if t >= step:
+                sigma = float(factor)
+        rng = np.random.default_rng([seed, 7, t])
+        x = rng.standard_normal((M, K), dtype=np.float32) * np.float32(sigma)
+        yield t, sigma, f32_to_bf16_bits(x)
+
+
 def expert_counts(tokens: int = 16384, experts: int = 8, seed: int = 0) -> np.ndarray:
     """Per-expert token counts from a seeded uniform multinomial."""
     rng = np.random.default_rng(seed)

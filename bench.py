@@ -17,6 +17,9 @@ seeded synthetic inputs already resident in HBM:
   payload    FP8 token messages for the dispatch of X 4096x7168 to top-2 of
              8 experts (8192 messages of 7392 bytes, gathered in expert
              order): pack, unpack into the GEMM operand layout, restore BF16
+  granularity  1xT quantization of X 8192x7168 for T = 32..1024 (the scale
+             metadata cost, 4/T bytes per value) and clipping at the 2nd
+             largest |x| of 1x128 tiles
   weights    128x128 quantization of W 18432x7168 with the transposed copy
   policy     one caller-scale (history policy) quantization of a 128x7168 tile
              with amax and saturation count, plus the history update
@@ -164,7 +167,7 @@ def main():
     # ---------------- inputs (seeded, synthetic, resident in HBM) ----------------
     t0 = time.time()
     d = {}
-    if want("quantizer"):
+    if want("quantizer") or want("granularity"):
         d["x2"] = to_dev(syn.activation_with_outliers(8192, 7168, seed=0), torch)
     host = {}
     if want("fprop") or want("backward") or want("weights"):
@@ -237,6 +240,10 @@ def main():
             tm.region("grouped.gemm", lambda: fp8.block_gemm_grouped(d["off5"], q, s, d["wq5"], d["ws5"]))
             ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
             tm.pending.append(("grouped", ev0, ev1))
+        if want("granularity"):
+            for T in (32, 64, 128, 256, 512, 1024):
+                tm.region(f"tiles.{T}", lambda T=T: fp8.quant_act_tiles(d["x2"], T, 1))
+            tm.region("tiles.128.rank2", lambda: fp8.quant_act_tiles(d["x2"], 128, 2))
         if want("payload"):
             tm.region("payload.pack", lambda: fp8.pack_tokens(d["x3"], d["src6"], out=d["msg6"]))
             tm.region("payload.unpack", lambda: fp8.unpack_tokens(d["msg6"], 7168))
@@ -358,6 +365,15 @@ def main():
         B = 18432 * 7168 * 4 + (18432 // 128) * (7168 // 128) * 4
         t = tm.mean_ms("weights")
         rows["weights"] = {"ms": t, "GB/s": B / t / 1e6}
+    if want("granularity"):
+        EL = 8192 * 7168
+        g = {}
+        for T in (32, 64, 128, 256, 512, 1024):
+            t = tm.mean_ms(f"tiles.{T}")
+            g[f"T{T}"] = {"ms": t, "GB/s": EL * (3 + 4 / T) / t / 1e6, "scale_bytes_per_value": 4 / T}
+        t = tm.mean_ms("tiles.128.rank2")
+        g["T128_rank2"] = {"ms": t, "GB/s": EL * (3 + 4 / 128) / t / 1e6}
+        rows["granularity"] = g
     if want("payload"):
         n_msg, MB = 8192, 7392
         tp, tu, tdq = tm.mean_ms("payload.pack"), tm.mean_ms("payload.unpack"), tm.mean_ms("payload.dequant")

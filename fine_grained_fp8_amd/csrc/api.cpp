@@ -206,6 +206,34 @@ fp8_status fp8_dequant_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t 
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
+fp8_status fp8_quant_act_tiles(const void* x, int64_t rows, int64_t cols, int64_t ldx, int32_t tile,
+                               int32_t rank, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                               uint32_t* sat_count, void* stream) {
+  if (!(tile == 32 || tile == 64 || tile == 128 || tile == 256 || tile == 512 || tile == 1024) ||
+      rank < 1 || rank > 8)
+    return FP8_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0 || cols % tile != 0) return FP8_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP8_OK;
+  if (!x || !q || !scales) return FP8_ERR_NULL;
+  if (ldx < cols || ldq < cols || ld_s < rows) return FP8_ERR_LD;
+  if (!aligned16(x) || !aligned16(q) || (ldx * 2) % 16 != 0 || ldq % 16 != 0 || !aligned4(scales) ||
+      !aligned4(sat_count))
+    return FP8_ERR_ALIGN;
+  const Range rx = span(x, rows, cols * 2, ldx * 2);
+  const Range rq = span(q, rows, cols, ldq);
+  const Range rs = span(scales, cols / tile, rows * 4, ld_s * 4);
+  if (overlap(rq, rx) || overlap(rs, rx) || overlap(rq, rs)) return FP8_ERR_ALIAS;
+  if (sat_count) {
+    const Range rc = span(sat_count, 1, 4, 4);
+    if (overlap(rc, rx) || overlap(rc, rq) || overlap(rc, rs)) return FP8_ERR_ALIAS;
+  }
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  return launched(fp8bs::launch_quant_tiles(static_cast<const uint16_t*>(x), rows, cols, ldx, tile, rank,
+                                            q, ldq, scales, ld_s, sat_count,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 fp8_status fp8_gemm_promotion(const uint8_t* A, int64_t M, int64_t K, int64_t lda, const uint8_t* B,
                               int64_t N, int64_t ldb, int64_t promote_k, float* C, int64_t ldc,
                               void* stream) {

@@ -42,6 +42,10 @@ hipError_t launch_unpack_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_
 hipError_t launch_dequant_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t stride,
                                  uint16_t* y, int64_t ldy, hipStream_t stream);
 
+hipError_t launch_quant_tiles(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int tile,
+                              int rank, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                              uint32_t* sat_count, hipStream_t stream);
+
 hipError_t launch_gemm_promotion(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
                                  int64_t M, int64_t N, int64_t K, int64_t promote_k, float* C,
                                  int64_t ldc, hipStream_t stream);

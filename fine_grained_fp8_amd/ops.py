@@ -277,3 +277,19 @@ def gemm_promotion(A: torch.Tensor, B: torch.Tensor, promote_k: int, *, stream=N
                                 _ptr(C), C.stride(0), _stream(stream))
     _lib.check("fp8_gemm_promotion", st)
     return C
+
+
+def quant_act_tiles(x: torch.Tensor, tile: int = 128, rank: int = 1, *, sat_count=None, stream=None):
+    """1 x tile quantization of x [rows][cols] BF16 with the clip value at the
+    rank-th largest |x| of each tile (rank 1: the max).  Returns
+    (q [rows][cols] uint8, scales [cols/tile][round_up(rows, 4)] float32).
+    sat_count: optional one-element int32/uint32 device tensor, incremented."""
+    lib = _lib.load_library()
+    _check_2d("x", x, _BF16)
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((cols // tile, round_up(rows, 4)), dtype=torch.float32, device=x.device)
+    st = lib.fp8_quant_act_tiles(_ptr(x), rows, cols, x.stride(0), tile, rank, _ptr(q), q.stride(0),
+                                 _ptr(s), s.stride(0), _ptr(sat_count), _stream(stream))
+    _lib.check("fp8_quant_act_tiles", st)
+    return q, s

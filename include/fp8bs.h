@@ -230,6 +230,27 @@ fp8_status fp8_amax_history_update(float* hist, const float* amax, int64_t n, fl
 fp8_status fp8_cast_e4m3(const float* x, int64_t n, uint8_t* q, void* stream);
 
 /*
+ * fp8_quant_act_tiles - the online rule with a chosen tile size and
+ * percentile clipping ("Fine-Grained FP8 Quantization in DeepSeek", section
+ * 2 and its study lab: error against tile size, scale metadata cost;
+ * "Online Quantization During Training", section 4: percentile clipping).
+ *  x       BF16 [rows][ldx >= cols]; cols % tile == 0.
+ *  tile    T in {32, 64, 128, 256, 512, 1024}: tiles of 1 x T contiguous
+ *          values of a row.
+ *  rank    1..8: the clip value c is the rank-th largest |x| of the tile
+ *          (1 = the max: with T = 128 the output equals fp8_quant_act_1x128
+ *          ROW); s = max(fl32(c / 448), fl32(1e-12)); the rank - 1 values
+ *          above c saturate.  A tile holding NaN: scale NaN, codes NaN.
+ *  q       [rows][ldq >= cols] codes;  scales [cols/T][ld_s >= rows] FP32.
+ *  sat_count  optional device uint32, incremented by the number of values
+ *          with |fl32(x / s)| > 464 (Inf included, NaN not); caller zeroes it.
+ *  Other tile or rank values: FP8_ERR_UNSUPPORTED.
+ */
+fp8_status fp8_quant_act_tiles(const void* x, int64_t rows, int64_t cols, int64_t ldx, int32_t tile,
+                               int32_t rank, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                               uint32_t* sat_count, void* stream);
+
+/*
  * fp8_gemm_promotion - accumulation-precision study: C = A . B^T over E4M3
  * codes with unit scales, FP32 out, with a chosen promotion interval
  * ("Introduction to LLM Quantization", section 3: tensor cores keep FP8 sums

@@ -199,6 +199,27 @@ def test_payload_validation(lib):
     assert deq() in (DEVICE, OK)
 
 
+def test_quant_tiles_validation(lib):
+    f = lambda x=X, rows=64, cols=2048, ldx=2048, tile=128, rank=1, q=Q, ldq=2048, s=S, lds=64, sat=None: \
+        lib.fp8_quant_act_tiles(x, rows, cols, ldx, tile, rank, q, ldq, s, lds, sat, None)
+    for tile in (0, 16, 100, 2048):
+        assert f(tile=tile) == UNSUP
+    for rank in (0, 9, -1):
+        assert f(rank=rank) == UNSUP
+    assert f(cols=2048 + 32, ldx=2080, ldq=2080) == SHAPE     # not a multiple of 128
+    assert f(tile=32, cols=2080, ldx=2080, ldq=2080) in (DEVICE, OK)
+    assert f(rows=0, x=None) == OK
+    assert f(q=None) == NULL
+    assert f(lds=60) == LD
+    assert f(ldq=1024) == LD
+    assert f(ldq=2056) == ALIGN
+    assert f(sat=A + 2) == ALIGN
+    assert f(q=X + 64) == ALIAS
+    assert f(sat=Q) == ALIAS
+    for tile in (32, 64, 128, 256, 512, 1024):
+        assert f(tile=tile, rank=8) in (DEVICE, OK)
+
+
 def test_gemm_promotion_validation(lib):
     f = lambda A_=A, M=64, K=256, lda=256, B_=B, N=48, ldb=256, pk=128, C_=C, ldc=48: \
         lib.fp8_gemm_promotion(A_, M, K, lda, B_, N, ldb, pk, C_, ldc, None)

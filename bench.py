@@ -5,11 +5,14 @@ seeded synthetic inputs already resident in HBM:
 
   quantizer  1x128 online quantization of X 8192x7168 (outliers in 16 channels)
   fprop      1x128 quantization of X 4096x7168 + block-scaled GEMM
-             Y = X W^T 4096x18432x7168 (W pre-quantized 128x128), BF16 out
+             Y = X W^T 4096x18432x7168 (W pre-quantized 128x128, codes in the
+             GEMM's operand-tiled layout), BF16 out; also timed with
+             row-major weight codes
   backward   dY 4096x18432 quantized in both orientations from one read
              (1x128 rows for Dgrad, 128x1 columns for Wgrad); Dgrad dX = dY W
              from the transposed weight codes W_q^T; 128x1 quantization of X +
-             Wgrad dW = dY^T X (FP32 out).  Also reported: Dgrad reading W_q
+             Wgrad dW = dY^T X (FP32 out).  Dgrad reads operand-tiled W_q^T
+             (also timed row-major).  Also reported: Dgrad reading W_q
              as stored ("dgrad_lds") and the dY quantization as two separate
              passes ("dual_quant")
   grouped    1x128 quantization of X 16384x7168 + one grouped launch over 8
@@ -20,7 +23,8 @@ seeded synthetic inputs already resident in HBM:
   granularity  1xT quantization of X 8192x7168 for T = 32..1024 (the scale
              metadata cost, 4/T bytes per value) and clipping at the 2nd
              largest |x| of 1x128 tiles
-  weights    128x128 quantization of W 18432x7168 with the transposed copy
+  weights    128x128 quantization of W 18432x7168 with the transposed copy,
+             both written operand-tiled
   policy     one caller-scale (history policy) quantization of a 128x7168 tile
              with amax and saturation count, plus the history update
   copy       a plain 1 GiB device-to-device copy (torch's copy kernel): the
@@ -177,7 +181,10 @@ def main():
         host["x3"] = syn.activation_with_outliers(4096, 7168, seed=0)
         d["x3"] = to_dev(host["x3"], torch)
     if want("fprop") or want("backward"):
-        d["wq3"], d["ws3"], d["wq3t"] = fp8.quant_weight_128x128(d["w3"], transposed=True)  # untimed
+        # untimed: the weight codes in the GEMM's operand-tiled layout (Fprop and
+        # Dgrad from W_q^T), and row-major for the comparison rows
+        d["wq3_tl"], d["ws3"], d["wq3t_tl"] = fp8.quant_weight_128x128(d["w3"], transposed=True, tiled=True)
+        d["wq3"], _, d["wq3t"] = fp8.quant_weight_128x128(d["w3"], transposed=True)
     if want("payload"):
         d["src6"] = to_dev(syn.dispatch_rows(4096, 8, 2, seed=5), torch)
         d["msg6"] = fp8.pack_tokens(d["x3"], d["src6"])
@@ -187,11 +194,14 @@ def main():
         counts = syn.expert_counts(16384, 8, seed=0)
         d["off5"] = to_dev(syn.expert_offsets(counts).astype(np.int32), torch)
         d["x5"] = to_dev(syn.activation_with_outliers(16384, 7168, seed=0), torch)
-        wq5, ws5 = [], []
+        wq5, ws5, wt5 = [], [], []
         for e in range(8):
-            q, s, _ = fp8.quant_weight_128x128(to_dev(syn.gaussian((2048, 7168), seed=100 + e, std=0.02), torch))
-            wq5.append(q); ws5.append(s)
+            we = to_dev(syn.gaussian((2048, 7168), seed=100 + e, std=0.02), torch)
+            q, s, _ = fp8.quant_weight_128x128(we)
+            qt, _, _ = fp8.quant_weight_128x128(we, tiled=True)
+            wq5.append(q); ws5.append(s); wt5.append(qt)
         d["wq5"] = torch.stack(wq5).contiguous()
+        d["wq5_tl"] = torch.stack(wt5).contiguous()
         d["ws5"] = torch.stack(ws5).contiguous()
         d["counts5"] = counts
     if want("policy"):
@@ -214,20 +224,23 @@ def main():
         if want("fprop"):
             ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
             q, s, _ = tm.region("fprop.quant", lambda: fp8.quant_act_1x128(d["x3"], "row"))
-            tm.region("fprop.gemm", lambda: fp8.block_gemm("fprop", q, s, d["wq3"], d["ws3"]))
+            tm.region("fprop.gemm", lambda: fp8.block_gemm("fprop_tiled", q, s, d["wq3_tl"], d["ws3"]))
             ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
             tm.pending.append(("fprop", ev0, ev1))
+            # the same GEMM reading row-major weight codes, for comparison
+            tm.region("fprop_rowmajor.gemm", lambda: fp8.block_gemm("fprop", q, s, d["wq3"], d["ws3"]))
         if want("backward"):
             ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
             # dY in both orientations from one read (Dgrad rows, Wgrad columns)
             dq, ds, dqt, dst = tm.region("bwd.quant_dual", lambda: fp8.quant_act_dual(d["dy4"]))
-            tm.region("dgrad.gemm", lambda: fp8.block_gemm("dgrad_t", dq, ds, d["wq3t"], d["ws3"]))
+            tm.region("dgrad.gemm", lambda: fp8.block_gemm("dgrad_t_tiled", dq, ds, d["wq3t_tl"], d["ws3"]))
             tm.region("dgrad_lds.gemm", lambda: fp8.block_gemm("dgrad", dq, ds, d["wq3"], d["ws3"]))
             xqt, xst, _ = tm.region("wgrad.quant_x", lambda: fp8.quant_act_1x128(d["x3"], "col"))
             tm.region("wgrad.gemm", lambda: fp8.block_gemm("wgrad", dqt, dst, xqt, xst,
                                                            out_dtype=torch.float32))
             ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
             tm.pending.append(("backward", ev0, ev1))
+            tm.region("dgrad_rowmajor.gemm", lambda: fp8.block_gemm("dgrad_t", dq, ds, d["wq3t"], d["ws3"]))
             # the same two quantizations as separate passes, for comparison
             tm.region("bwd.quant_row", lambda: fp8.quant_act_1x128(d["dy4"], "row"))
             tm.region("bwd.quant_col", lambda: fp8.quant_act_1x128(d["dy4"], "col"))
@@ -237,9 +250,11 @@ def main():
         if want("grouped"):
             ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
             q, s, _ = tm.region("grouped.quant", lambda: fp8.quant_act_1x128(d["x5"], "row"))
-            tm.region("grouped.gemm", lambda: fp8.block_gemm_grouped(d["off5"], q, s, d["wq5"], d["ws5"]))
+            tm.region("grouped.gemm", lambda: fp8.block_gemm_grouped(d["off5"], q, s, d["wq5_tl"], d["ws5"],
+                                                                     tiled=True))
             ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
             tm.pending.append(("grouped", ev0, ev1))
+            tm.region("grouped_rowmajor.gemm", lambda: fp8.block_gemm_grouped(d["off5"], q, s, d["wq5"], d["ws5"]))
         if want("granularity"):
             for T in (32, 64, 128, 256, 512, 1024):
                 tm.region(f"tiles.{T}", lambda T=T: fp8.quant_act_tiles(d["x2"], T, 1))
@@ -249,7 +264,7 @@ def main():
             tm.region("payload.unpack", lambda: fp8.unpack_tokens(d["msg6"], 7168))
             tm.region("payload.dequant", lambda: fp8.dequant_tokens(d["msg6"], 7168))
         if want("weights"):
-            tm.region("weights", lambda: fp8.quant_weight_128x128(d["w3"], transposed=True))
+            tm.region("weights", lambda: fp8.quant_weight_128x128(d["w3"], transposed=True, tiled=True))
         if want("policy"):
             def pol():
                 fp8.quant_act_1x128(d["xp"], "row", scales_in=d["sp"], return_amax=True,
@@ -306,7 +321,7 @@ def main():
         del xs
     if want("fprop"):
         q3, s3, _ = fp8.quant_act_1x128(d["x3"], "row")
-        batch["fprop.gemm"] = batch_ms(lambda: fp8.block_gemm("fprop", q3, s3, d["wq3"], d["ws3"]), 5)
+        batch["fprop.gemm"] = batch_ms(lambda: fp8.block_gemm("fprop_tiled", q3, s3, d["wq3_tl"], d["ws3"]), 5)
     log("batches: " + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in batch.items()))
     log(f"timed {args.steps} steps: {steps_ms:.2f} ms on the GPU, {wall:.2f} s wall")
 
@@ -323,14 +338,17 @@ def main():
     if want("fprop"):
         tq, tg, tt = tm.mean_ms("fprop.quant"), tm.mean_ms("fprop.gemm"), tm.mean_ms("fprop")
         value = F3 / (tq + tg) / 1e9
+        trm = tm.mean_ms("fprop_rowmajor.gemm")
         rows["fprop"] = {"ms_quant": tq, "ms_gemm": tg, "ms_region": tt,
                          "TFLOP/s_incl_quant": value, "TFLOP/s_gemm": F3 / tg / 1e9,
-                         "quant_GB/s": 4096 * 7168 * (3 + 4 / 128) / tq / 1e6}
+                         "quant_GB/s": 4096 * 7168 * (3 + 4 / 128) / tq / 1e6,
+                         "weights": "operand-tiled codes",
+                         "ms_gemm_rowmajor_weights": trm, "TFLOP/s_gemm_rowmajor_weights": F3 / trm / 1e9}
         achieved = F3 / batch["fprop.gemm"] / 1e9
         traffic = traffic_from_profiles("fprop_gemm_traffic.json", "fine_grained_fp8_amd/csrc/gemm.hip")
         roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": traffic,
-                    "kernel": "block_gemm_direct_kernel<FPROP,bf16> 4096x18432x7168",
+                    "kernel": "block_gemm_direct_kernel<FPROP,bf16,tiled weights> 4096x18432x7168",
                     "algorithmic_flop_per_launch": F3, "ms_per_launch": batch["fprop.gemm"],
                     "timing": "5 back-to-back launches between HIP events on the launch stream"}
     if want("backward"):
@@ -349,8 +367,10 @@ def main():
                                 "ms_separate_row_plus_col": tsx, "speedup_vs_separate": tsx / tdx}
         # each GEMM is charged the share of the dual pass its operand costs
         tq1 = tq2 = tdual / 2
+        tdr = tm.mean_ms("dgrad_rowmajor.gemm")
         rows["dgrad"] = {"ms_quant_share": tq1, "ms_gemm": tg1, "TFLOP/s_incl_quant": F3 / (tq1 + tg1) / 1e9,
-                         "TFLOP/s_gemm": F3 / tg1 / 1e9, "layout": "dgrad_t (W_q^T)"}
+                         "TFLOP/s_gemm": F3 / tg1 / 1e9, "layout": "dgrad_t_tiled (W_q^T, operand-tiled)",
+                         "ms_gemm_rowmajor_weights": tdr, "TFLOP/s_gemm_rowmajor_weights": F3 / tdr / 1e9}
         tl = tm.mean_ms("dgrad_lds.gemm")
         rows["dgrad_lds"] = {"ms_gemm": tl, "TFLOP/s_gemm": F3 / tl / 1e9, "layout": "dgrad (W_q read transposed)"}
         rows["wgrad"] = {"ms_quant_dy_share": tq2, "ms_quant_x_col": tq3, "ms_gemm": tg2,
@@ -359,8 +379,11 @@ def main():
     if want("grouped"):
         F5 = 2.0 * 16384 * 2048 * 7168
         tq, tg = tm.mean_ms("grouped.quant"), tm.mean_ms("grouped.gemm")
+        tgr = tm.mean_ms("grouped_rowmajor.gemm")
         rows["grouped"] = {"ms_quant": tq, "ms_gemm": tg, "TFLOP/s_incl_quant": F5 / (tq + tg) / 1e9,
-                           "TFLOP/s_gemm": F5 / tg / 1e9, "tokens_per_expert": [int(c) for c in d["counts5"]]}
+                           "TFLOP/s_gemm": F5 / tg / 1e9, "tokens_per_expert": [int(c) for c in d["counts5"]],
+                           "weights": "operand-tiled codes",
+                           "ms_gemm_rowmajor_weights": tgr, "TFLOP/s_gemm_rowmajor_weights": F5 / tgr / 1e9}
     if want("weights"):
         B = 18432 * 7168 * 4 + (18432 // 128) * (7168 // 128) * 4
         t = tm.mean_ms("weights")

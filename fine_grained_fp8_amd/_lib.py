@@ -17,7 +17,7 @@ STATUS = {
     5: "FP8_ERR_UNSUPPORTED", 6: "FP8_ERR_DEVICE", 7: "FP8_ERR_LAUNCH", 8: "FP8_ERR_ALIAS",
 }
 TILE_ROW, TILE_COL = 0, 1
-LAYOUT = {"fprop": 0, "dgrad": 1, "wgrad": 2, "dgrad_t": 3}
+LAYOUT = {"fprop": 0, "dgrad": 1, "wgrad": 2, "dgrad_t": 3, "fprop_tiled": 4, "dgrad_t_tiled": 5}
 OUT_BF16, OUT_FP32 = 0, 1
 
 # name -> (restype, argtypes); mirrors include/fp8bs.h
@@ -33,6 +33,9 @@ SIGNATURES = {
     "fp8_quant_weight_128x128": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
     "fp8_block_gemm": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P,
                                       _I64, _P, ctypes.c_int, _I64, _P]),
+    "fp8_quant_weight_128x128_tiled": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P]),
+    "fp8_block_gemm_grouped_tiled": (ctypes.c_int, [_I32, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P,
+                                                    _P, _P, ctypes.c_int, _I64, _P]),
     "fp8_block_gemm_grouped": (ctypes.c_int, [_I32, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64,
                                               _P, _P, ctypes.c_int, _I64, _P]),
     "fp8_amax_history_update": (ctypes.c_int, [_P, _P, _I64, _F, ctypes.c_int, _P, _P]),

@@ -253,9 +253,10 @@ fp8_status fp8_gemm_promotion(const uint8_t* A, int64_t M, int64_t K, int64_t ld
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
-fp8_status fp8_quant_weight_128x128(const void* w, int64_t rows, int64_t cols, int64_t ldw,
-                                    uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
-                                    float* scales, int64_t ld_s, void* stream) {
+namespace {
+fp8_status quant_weight_impl(const void* w, int64_t rows, int64_t cols, int64_t ldw, uint8_t* q,
+                             int64_t ldq, uint8_t* q_t, int64_t ldq_t, float* scales, int64_t ld_s,
+                             bool tiled, void* stream) {
   if (rows < 0 || cols < 0 || rows % 128 != 0 || cols % 128 != 0) return FP8_ERR_SHAPE;
   if (rows == 0 || cols == 0) return FP8_OK;
   if (!w || !q || !scales) return FP8_ERR_NULL;
@@ -274,8 +275,23 @@ fp8_status fp8_quant_weight_128x128(const void* w, int64_t rows, int64_t cols, i
   const fp8_status dev = check_device();
   if (dev != FP8_OK) return dev;
   return launched(fp8bs::launch_quant_weight(static_cast<const uint16_t*>(w), rows, cols, ldw, q, ldq,
-                                             q_t, ldq_t, scales, ld_s,
+                                             q_t, ldq_t, scales, ld_s, tiled,
                                              reinterpret_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+fp8_status fp8_quant_weight_128x128(const void* w, int64_t rows, int64_t cols, int64_t ldw,
+                                    uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
+                                    float* scales, int64_t ld_s, void* stream) {
+  return quant_weight_impl(w, rows, cols, ldw, q, ldq, q_t, ldq_t, scales, ld_s, false, stream);
+}
+
+fp8_status fp8_quant_weight_128x128_tiled(const void* w, int64_t rows, int64_t cols, int64_t ldw,
+                                          uint8_t* q_tiled, uint8_t* q_t_tiled, float* scales,
+                                          int64_t ld_s, void* stream) {
+  // the tiled arrays are dense: rows * cols bytes each
+  return quant_weight_impl(w, rows, cols, ldw, q_tiled, cols, q_t_tiled, rows, scales, ld_s, true,
+                           stream);
 }
 
 static fp8_status validate_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* A,
@@ -301,8 +317,11 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
                           const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
                           void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream) {
   if (layout != FP8_LAYOUT_FPROP && layout != FP8_LAYOUT_DGRAD && layout != FP8_LAYOUT_WGRAD &&
-      layout != FP8_LAYOUT_DGRAD_T)
+      layout != FP8_LAYOUT_DGRAD_T && layout != FP8_LAYOUT_FPROP_TILED &&
+      layout != FP8_LAYOUT_DGRAD_T_TILED)
     return FP8_ERR_UNSUPPORTED;
+  const bool tiled = layout == FP8_LAYOUT_FPROP_TILED || layout == FP8_LAYOUT_DGRAD_T_TILED;
+  if (tiled) layout = layout == FP8_LAYOUT_FPROP_TILED ? FP8_LAYOUT_FPROP : FP8_LAYOUT_DGRAD_T;
   fp8_status st = validate_gemm_common(M, N, K, A, lda, sA, ld_sa, B, sB, C, c_dtype, ldc);
   if (st != FP8_OK || M == 0) return st;
   if (layout != FP8_LAYOUT_WGRAD && N % 128 != 0) return FP8_ERR_SHAPE;
@@ -314,6 +333,7 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
     default: b_rows = N; b_cols = K; sb_rows = K / 128; sb_cols = N; break;
   }
   if (ldb < b_cols || ld_sb < sb_cols) return FP8_ERR_LD;
+  if (tiled && ldb != K) return FP8_ERR_LD;       // dense tiles: the row "stride" is K
   if (ldb % 16 != 0) return FP8_ERR_ALIGN;
   if (ldb > (int64_t{1} << 23)) return FP8_ERR_UNSUPPORTED;
   if (layout == FP8_LAYOUT_DGRAD && K * ldb >= (int64_t{1} << 31)) return FP8_ERR_UNSUPPORTED;
@@ -333,22 +353,23 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
   p.A = A; p.lda = lda; p.sA = sA; p.ld_sa = ld_sa;
   p.B = B; p.ldb = ldb; p.sB = sB; p.ld_sb = ld_sb;
   p.C = C; p.ldc = ldc; p.out_fp32 = c_dtype == FP8_OUT_FP32;
+  p.b_tiled = tiled ? 1 : 0;
   p.groups = 0; p.offsets = nullptr;
   return launched(fp8bs::launch_gemm(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
-fp8_status fp8_block_gemm_grouped(int32_t groups, const int32_t* offsets_dev, int64_t total_M,
-                                  int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-                                  const float* sA, int64_t ld_sa, const uint8_t* B, int64_t ldb,
-                                  const float* sB, void* C, fp8_out_dtype c_dtype, int64_t ldc,
-                                  void* stream) {
+namespace {
+fp8_status grouped_impl(int32_t groups, const int32_t* offsets_dev, int64_t total_M, int64_t N,
+                        int64_t K, const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
+                        const uint8_t* B, int64_t ldb, const float* sB, void* C,
+                        fp8_out_dtype c_dtype, int64_t ldc, bool tiled, void* stream) {
   if (groups <= 0) return FP8_ERR_SHAPE;
   fp8_status st = validate_gemm_common(total_M, N, K, A, lda, sA, ld_sa, B, sB, C, c_dtype, ldc);
   if (st != FP8_OK || total_M == 0) return st;
   if (!offsets_dev) return FP8_ERR_NULL;
   if (!aligned4(offsets_dev)) return FP8_ERR_ALIGN;
   if (N % 128 != 0) return FP8_ERR_SHAPE;
-  if (ldb < K) return FP8_ERR_LD;
+  if (ldb < K || (tiled && ldb != K)) return FP8_ERR_LD;
   if (ldb % 16 != 0) return FP8_ERR_ALIGN;
   if (ldb > (int64_t{1} << 23)) return FP8_ERR_UNSUPPORTED;
   if ((N / 128) * (K / 128) >= (int64_t{1} << 29)) return FP8_ERR_UNSUPPORTED;
@@ -368,8 +389,28 @@ fp8_status fp8_block_gemm_grouped(int32_t groups, const int32_t* offsets_dev, in
   p.A = A; p.lda = lda; p.sA = sA; p.ld_sa = ld_sa;
   p.B = B; p.ldb = ldb; p.sB = sB; p.ld_sb = K / 128;
   p.C = C; p.ldc = ldc; p.out_fp32 = c_dtype == FP8_OUT_FP32;
+  p.b_tiled = tiled ? 1 : 0;
   p.groups = groups; p.offsets = offsets_dev;
   return launched(fp8bs::launch_gemm(p, reinterpret_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+fp8_status fp8_block_gemm_grouped(int32_t groups, const int32_t* offsets_dev, int64_t total_M,
+                                  int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                  const float* sA, int64_t ld_sa, const uint8_t* B, int64_t ldb,
+                                  const float* sB, void* C, fp8_out_dtype c_dtype, int64_t ldc,
+                                  void* stream) {
+  return grouped_impl(groups, offsets_dev, total_M, N, K, A, lda, sA, ld_sa, B, ldb, sB, C, c_dtype,
+                      ldc, false, stream);
+}
+
+fp8_status fp8_block_gemm_grouped_tiled(int32_t groups, const int32_t* offsets_dev, int64_t total_M,
+                                        int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                        const float* sA, int64_t ld_sa, const uint8_t* B,
+                                        const float* sB, void* C, fp8_out_dtype c_dtype,
+                                        int64_t ldc, void* stream) {
+  return grouped_impl(groups, offsets_dev, total_M, N, K, A, lda, sA, ld_sa, B, K, sB, C, c_dtype,
+                      ldc, true, stream);
 }
 
 fp8_status fp8_amax_history_update(float* hist, const float* amax, int64_t n, float decay,

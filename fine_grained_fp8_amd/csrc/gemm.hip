@@ -466,7 +466,7 @@ constexpr int kDDmaOps = 4 + 1 + 1;            // DMA per block: 4 token-row, 2 
 constexpr int kDWOps = 8;                      // weight loads per block
 constexpr int kDOpsPerBlock = kDDmaOps + kDWOps;
 
-template <int kLayout, bool kOutF32, bool kGrouped>
+template <int kLayout, bool kOutF32, bool kGrouped, bool kTiledB>
 __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProblem p, int64_t total_tiles) {
   static_assert(kLayout != kDgrad, "Dgrad reads the weights transposed through LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s0[kDStage];
@@ -496,8 +496,13 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   // weight-side rows n0 + 64 wave + 16 i + lrow, loaded straight into registers
   const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(Bp + n0 * p.ldb), (short)0, rows_n * (int)p.ldb, (int)kRsrcWord3);
-  const uint32_t off_w = (uint32_t)((wave * 64 + lrow) * (int)p.ldb + lgrp * 16);
-  const uint32_t w_istride = (uint32_t)(16 * p.ldb);
+  // row-major: lane reads 16 B of its row; operand-tiled (ldb == K): the
+  // wave's 16-row groups are 2 KB tiles per K block, each half one 1 KB run
+  const uint32_t off_w = kTiledB ? (uint32_t)(wave * 4 * KB * 2048 + lane * 16)
+                                 : (uint32_t)((wave * 64 + lrow) * (int)p.ldb + lgrp * 16);
+  const uint32_t w_istride = kTiledB ? (uint32_t)(KB * 2048) : (uint32_t)(16 * p.ldb);
+  const uint32_t w_hstride = kTiledB ? 1024u : 64u;
+  const uint32_t w_kstride = kTiledB ? 2048u : (uint32_t)BK;
   // weight-side scales: Fprop / Dgrad_T - the wave's 128x128 weight block
   // (every lane fetches the same float; Fprop's table is [N/128][K/128],
   // Dgrad_T reads the forward table [K/128][N/128]); Wgrad - the workgroup's
@@ -531,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     } else {
       const int i = (op - 6) >> 1, h = (op - 6) & 1;
       const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
-          rsrc_w, off_w + (uint32_t)i * w_istride + (uint32_t)(h * 64 + kb * BK), 0, 0);
+          rsrc_w, off_w + (uint32_t)i * w_istride + (uint32_t)h * w_hstride + (uint32_t)kb * w_kstride, 0, 0);
       wr[i][4 * h + 0] = v[0];
       wr[i][4 * h + 1] = v[1];
       wr[i][4 * h + 2] = v[2];
@@ -701,12 +706,30 @@ hipError_t launch_typed(const GemmProblem& p, hipStream_t stream, int64_t grid, 
       hipLaunchKernelGGL((block_gemm_kernel<kLayout, false, kGrouped>), dim3((unsigned)grid),
                          dim3(kThreads), 0, stream, p, total);
     }
+  } else if constexpr (kLayout != kWgrad) {
+    if (p.b_tiled) {
+      if (p.out_fp32) {
+        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped, true>), dim3((unsigned)grid),
+                           dim3(kThreads), 0, stream, p, total);
+      } else {
+        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped, true>), dim3((unsigned)grid),
+                           dim3(kThreads), 0, stream, p, total);
+      }
+    } else {
+      if (p.out_fp32) {
+        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped, false>), dim3((unsigned)grid),
+                           dim3(kThreads), 0, stream, p, total);
+      } else {
+        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped, false>), dim3((unsigned)grid),
+                           dim3(kThreads), 0, stream, p, total);
+      }
+    }
   } else {
     if (p.out_fp32) {
-      hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped, false>), dim3((unsigned)grid),
                          dim3(kThreads), 0, stream, p, total);
     } else {
-      hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped, false>), dim3((unsigned)grid),
                          dim3(kThreads), 0, stream, p, total);
     }
   }

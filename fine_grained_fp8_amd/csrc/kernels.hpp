@@ -24,7 +24,7 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
 
 hipError_t launch_quant_weight(const uint16_t* w, int64_t rows, int64_t cols, int64_t ldw,
                                uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
-                               float* scales, int64_t ld_s, hipStream_t stream);
+                               float* scales, int64_t ld_s, bool tiled, hipStream_t stream);
 
 hipError_t launch_history_update(float* hist, const float* amax, int64_t n, float decay, int init,
                                  float* scales_out, hipStream_t stream);
@@ -66,6 +66,7 @@ struct GemmProblem {
   void* C;
   int64_t ldc;
   int out_fp32;
+  int b_tiled;           // B in the operand-tiled layout (FPROP, DGRAD_T, grouped; ldb == K)
   // grouped FPROP: groups > 0
   int groups;
   const int32_t* offsets;

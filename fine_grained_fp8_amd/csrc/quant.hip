@@ -309,10 +309,15 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
 // ---------------------------------------------------------------------------
 // 128x128 weight blocks: one workgroup per block, block max through DPP row
 // reduction, cross-row shuffles and LDS; optional transposed codes via an LDS
-// byte tile and 4x4 byte transposes (for the input-gradient GEMM).
+// byte tile and 4x4 byte transposes (for the input-gradient GEMM).  kTiled
+// writes both code matrices in the GEMM's operand-tiled layout instead of
+// row-major: per 16 rows x 128 columns one 2 KB tile, whose 1 KB halves are
+// what a wave's 64 lanes load as 16 bytes each (lane 16g + i: row i, columns
+// 64h + 16g..).
 // ---------------------------------------------------------------------------
+template <bool kTiled>
 __global__ __launch_bounds__(256) void quant_weight_kernel(
-    const uint16_t* __restrict__ w, int64_t ldw, int64_t nbk,
+    const uint16_t* __restrict__ w, int64_t ldw, int64_t nbk, int64_t nbr,
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ q_t, int64_t ldq_t,
     float* __restrict__ scales, int64_t ld_s) {
   __shared__ uint32_t wmax[4];
@@ -355,7 +360,16 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
       out.x = pack4_sat_nan(bf16_lo(d.x) / s, bf16_hi(d.x) / s, bf16_lo(d.y) / s, bf16_hi(d.y) / s);
       out.y = pack4_sat_nan(bf16_lo(d.z) / s, bf16_hi(d.z) / s, bf16_lo(d.w) / s, bf16_hi(d.w) / s);
     }
-    *reinterpret_cast<uint2*>(q + (r0 + row) * ldq + c0 + cc * 8) = out;
+    if constexpr (kTiled) {
+      // operand-tiled: 2 KB per 16 rows x 128 columns; this chunk (columns
+      // 8cc..8cc+7 of the block) is half of lane slot (cc >> 1) & 3 of half cc >> 3
+      const int64_t R = r0 + row;
+      const int64_t off = ((R >> 4) * nbk + bj) * 2048 + (cc >> 3) * 1024 +
+                          ((((cc >> 1) & 3) << 4) + (R & 15)) * 16 + (cc & 1) * 8;
+      *reinterpret_cast<uint2*>(q + off) = out;
+    } else {
+      *reinterpret_cast<uint2*>(q + (r0 + row) * ldq + c0 + cc * 8) = out;
+    }
     if (q_t) {
       codes[row][cc * 2] = out.x;
       codes[row][cc * 2 + 1] = out.y;
@@ -374,7 +388,14 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const uint4 val = make_uint4(o[0][jj], o[1][jj], o[2][jj], o[3][jj]);
-    *reinterpret_cast<uint4*>(q_t + (c0 + 4 * cg + jj) * ldq_t + r0 + 16 * rg) = val;
+    if constexpr (kTiled) {
+      // row R of the transposed matrix, its K block bi, 16 columns 16rg..: one lane slot
+      const int64_t R = c0 + 4 * cg + jj;
+      const int64_t off = ((R >> 4) * nbr + bi) * 2048 + (rg >> 2) * 1024 + (((rg & 3) << 4) + (R & 15)) * 16;
+      *reinterpret_cast<uint4*>(q_t + off) = val;
+    } else {
+      *reinterpret_cast<uint4*>(q_t + (c0 + 4 * cg + jj) * ldq_t + r0 + 16 * rg) = val;
+    }
   }
 }
 
@@ -454,11 +475,15 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int6
 
 hipError_t launch_quant_weight(const uint16_t* w, int64_t rows, int64_t cols, int64_t ldw,
                                uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,
-                               float* scales, int64_t ld_s, hipStream_t stream) {
-  const int64_t nbk = cols / 128;
-  const int64_t nblocks = (rows / 128) * nbk;
-  hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream,
-                     w, ldw, nbk, q, ldq, q_t, ldq_t, scales, ld_s);
+                               float* scales, int64_t ld_s, bool tiled, hipStream_t stream) {
+  const int64_t nbk = cols / 128, nbr = rows / 128;
+  const int64_t nblocks = nbr * nbk;
+  if (tiled)
+    hipLaunchKernelGGL(quant_weight_kernel<true>, dim3((unsigned)nblocks), dim3(256), 0, stream,
+                       w, ldw, nbk, nbr, q, ldq, q_t, ldq_t, scales, ld_s);
+  else
+    hipLaunchKernelGGL(quant_weight_kernel<false>, dim3((unsigned)nblocks), dim3(256), 0, stream,
+                       w, ldw, nbk, nbr, q, ldq, q_t, ldq_t, scales, ld_s);
   return hipGetLastError();
 }
 

@@ -108,10 +108,13 @@ def quant_act_dual(x: torch.Tensor, *, stream=None):
     return q_row, s_row, q_col, s_col
 
 
-def quant_weight_128x128(w: torch.Tensor, *, transposed: bool = False, stream=None):
+def quant_weight_128x128(w: torch.Tensor, *, transposed: bool = False, tiled: bool = False,
+                         stream=None):
     """128x128 block quantization of weights [N][K].
 
     Returns (q [N][K] uint8, scales [N/128][K/128] float32, q_t [K][N] or None).
+    tiled: q (and q_t) hold the operand-tiled bytes of the same codes, for
+    the "fprop_tiled" / "dgrad_t_tiled" GEMM layouts (same shapes).
     """
     lib = _lib.load_library()
     _check_2d("w", w, _BF16)
@@ -119,6 +122,11 @@ def quant_weight_128x128(w: torch.Tensor, *, transposed: bool = False, stream=No
     q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
     q_t = torch.empty((cols, rows), dtype=torch.uint8, device=w.device) if transposed else None
     scales = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=w.device)
+    if tiled:
+        st = lib.fp8_quant_weight_128x128_tiled(_ptr(w), rows, cols, w.stride(0), _ptr(q), _ptr(q_t),
+                                                _ptr(scales), scales.stride(0), _stream(stream))
+        _lib.check("fp8_quant_weight_128x128_tiled", st)
+        return q, scales, q_t
     st = lib.fp8_quant_weight_128x128(
         _ptr(w), rows, cols, w.stride(0), _ptr(q), q.stride(0), _ptr(q_t),
         q_t.stride(0) if q_t is not None else 0, _ptr(scales), scales.stride(0), _stream(stream))
@@ -135,6 +143,8 @@ def block_gemm(layout: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, 
     dgrad_t: A [M][K], sA [K/128][>=M], B [N][K] (W_q^T, the q_t of the weight
              quantizer), sB [K/128][>=N/128] (the forward block-scale table)
     wgrad: A [M][K], sA [K/128][>=M], B [N][K], sB [K/128][>=N]
+    fprop_tiled / dgrad_t_tiled: as fprop / dgrad_t with B holding the
+             operand-tiled bytes (quant_weight_128x128(..., tiled=True))
     Returns C [M][N] in out_dtype (bfloat16 or float32).
     """
     lib = _lib.load_library()
@@ -156,11 +166,13 @@ def block_gemm(layout: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, 
 
 
 def block_gemm_grouped(offsets: torch.Tensor, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor,
-                       sB: torch.Tensor, *, out_dtype=torch.bfloat16, out=None, stream=None):
+                       sB: torch.Tensor, *, tiled: bool = False, out_dtype=torch.bfloat16, out=None,
+                       stream=None):
     """Grouped per-expert Fprop in one launch.
 
     offsets: int32 device [G+1]; A [total_M][K]; sA [K/128][>=total_M];
-    B [G][N][K]; sB [G][N/128][K/128].  Returns C [total_M][N].
+    B [G][N][K] (operand-tiled bytes per expert if tiled); sB [G][N/128][K/128].
+    Returns C [total_M][N].
     """
     lib = _lib.load_library()
     _check_2d("A", A, (torch.uint8, torch.float8_e4m3fn))
@@ -174,6 +186,12 @@ def block_gemm_grouped(offsets: torch.Tensor, A: torch.Tensor, sA: torch.Tensor,
     if out is None:
         out = torch.empty((total_M, N), dtype=out_dtype, device=A.device)
     code = _lib.OUT_FP32 if out.dtype == torch.float32 else _lib.OUT_BF16
+    if tiled:
+        st = lib.fp8_block_gemm_grouped_tiled(
+            G, _ptr(offsets), total_M, N, K, _ptr(A), A.stride(0), _ptr(sA), sA.stride(0),
+            _ptr(B), _ptr(sB), _ptr(out), code, out.stride(0), _stream(stream))
+        _lib.check("fp8_block_gemm_grouped_tiled", st)
+        return out
     st = lib.fp8_block_gemm_grouped(
         G, _ptr(offsets), total_M, N, K, _ptr(A), A.stride(0), _ptr(sA), sA.stride(0),
         _ptr(B), B.stride(1), _ptr(sB), _ptr(out), code, out.stride(0), _stream(stream))

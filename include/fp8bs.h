@@ -85,7 +85,9 @@ typedef enum {
   FP8_LAYOUT_FPROP = 0, /* C[M][N] = A[M][K] . B[N][K]^T,  B = W_q (weights [d_out][d_in]) */
   FP8_LAYOUT_DGRAD = 1, /* C[M][N] = A[M][K] . B[K][N],    B = W_q stored [d_out = K][d_in = N] */
   FP8_LAYOUT_WGRAD = 2, /* C[M][N] = A[M][K] . B[N][K]^T,  K = tokens, per-row x per-column scales */
-  FP8_LAYOUT_DGRAD_T = 3 /* C[M][N] = A[M][K] . B[N][K]^T,  B = W_q^T (transposed weight codes) */
+  FP8_LAYOUT_DGRAD_T = 3, /* C[M][N] = A[M][K] . B[N][K]^T,  B = W_q^T (transposed weight codes) */
+  FP8_LAYOUT_FPROP_TILED = 4,  /* FPROP with B in the operand-tiled layout (ldb == K) */
+  FP8_LAYOUT_DGRAD_T_TILED = 5 /* DGRAD_T with B in the operand-tiled layout (ldb == K) */
 } fp8_gemm_layout;
 
 typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_FP32 = 1 } fp8_out_dtype;
@@ -159,6 +161,25 @@ fp8_status fp8_quant_weight_128x128(const void* w, int64_t rows, int64_t cols, i
                                     float* scales, int64_t ld_s, void* stream);
 
 /*
+ * fp8_quant_weight_128x128_tiled - the same quantization with the codes
+ * written in the operand-tiled layout the GEMM's *_TILED layouts read
+ * ("Fine-Grained FP8 Quantization in DeepSeek", section 4: how operands and
+ * their scales are laid out decides real performance).  For a code matrix
+ * Q [R][C] the tiled array holds R * C bytes; element (r, c) is at
+ *     ((r / 16) * (C / 128) + c / 128) * 2048 + ((c % 128) / 64) * 1024
+ *       + (((c % 64) / 16) * 16 + r % 16) * 16 + c % 16
+ * so every 1 KB half of a 2 KB tile is one contiguous 16-byte-per-lane load
+ * of a wave.  The codes and scales equal fp8_quant_weight_128x128's.
+ *  q_tiled    [rows * cols] bytes: W_q tiled (R = rows, C = cols)
+ *  q_t_tiled  optional (NULL): W_q^T tiled (R = cols, C = rows), for
+ *             FP8_LAYOUT_DGRAD_T_TILED
+ *  scales     FP32 [rows/128][ld_s >= cols/128]
+ */
+fp8_status fp8_quant_weight_128x128_tiled(const void* w, int64_t rows, int64_t cols, int64_t ldw,
+                                          uint8_t* q_tiled, uint8_t* q_t_tiled, float* scales,
+                                          int64_t ld_s, void* stream);
+
+/*
  * fp8_block_gemm - block-scaled FP8 GEMM, FP32 accumulation, per-128-K scale
  * epilogue:
  *     C[m][n] = round( sum_kb  sa(m, kb) * sb(n, kb) * sum_{k in kb} A(m, k) * B(k, n) )
@@ -183,6 +204,10 @@ fp8_status fp8_quant_weight_128x128(const void* w, int64_t rows, int64_t cols, i
  *  FP8_LAYOUT_WGRAD   (M = d_out, N = d_in, K = tokens)
  *     A  = dY_q^T [M][lda >= K];   sA [K/128][ld_sa >= M]     (128x1 column scales)
  *     B  = X_q^T  [N][ldb >= K];   sB [K/128][ld_sb >= N]     (128x1 column scales)
+ *  FP8_LAYOUT_FPROP_TILED, FP8_LAYOUT_DGRAD_T_TILED - FPROP and DGRAD_T with B
+ *     in the operand-tiled layout of fp8_quant_weight_128x128_tiled (q_tiled,
+ *     resp. q_t_tiled); ldb must equal K.  Bit-identical results; the weight
+ *     loads become whole contiguous lines.
  *  C: [M][ldc >= N], BF16 (round to nearest even) or FP32 (c_dtype).
  *  M == 0 is a no-op.  C must not overlap A, B or the scales.
  */
@@ -210,6 +235,17 @@ fp8_status fp8_block_gemm_grouped(int32_t groups, const int32_t* offsets_dev, in
                                   const float* sA, int64_t ld_sa, const uint8_t* B, int64_t ldb,
                                   const float* sB, void* C, fp8_out_dtype c_dtype, int64_t ldc,
                                   void* stream);
+
+/*
+ * fp8_block_gemm_grouped_tiled - fp8_block_gemm_grouped with each expert's
+ * B_g in the operand-tiled layout (N * K bytes per expert, expert g at
+ * B + g * N * K); bit-identical results.
+ */
+fp8_status fp8_block_gemm_grouped_tiled(int32_t groups, const int32_t* offsets_dev, int64_t total_M,
+                                        int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                        const float* sA, int64_t ld_sa, const uint8_t* B,
+                                        const float* sB, void* C, fp8_out_dtype c_dtype,
+                                        int64_t ldc, void* stream);
 
 /*
  * fp8_amax_history_update - per-tile state of the exponential amax-history

@@ -255,3 +255,76 @@ def test_grouped_full_size_sampled(gpu_lib):
         R, T = og.fprop(Xq[rows], sX[rows], Wq_e[e], sW_e[e], with_magnitude=True)
         E = truncation_bound(Xq[rows], sX[rows], Wq_e[e], og.expand_block_scales(sW_e[e], 2048))
         check_gemm(y[rows], R, T, 7168, E=E, label=f"grouped expert {e}")
+
+
+# ---------------------------------------------------------------------------
+# Operand-tiled weight codes: the quantizer's tiled bytes against the
+# oracle's layout, and every tiled GEMM bit-identical to its row-major twin.
+# ---------------------------------------------------------------------------
+def test_tiled_weight_codes_match_the_layout(gpu_lib):
+    from oracle import tiling
+    wb = syn.gaussian((384, 640), seed=71, std=0.02)
+    Wq, sW = quant.quant_weight(wb)
+    q, s, q_t = gpu_lib.quant_weight_128x128(dev(wb), transposed=True, tiled=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy().ravel(), tiling.tile_codes(Wq))
+    assert np.array_equal(q_t.cpu().numpy().ravel(), tiling.tile_codes(np.ascontiguousarray(Wq.T)))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), sW.view(np.uint32))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_tiled_fprop_and_dgrad_t_bit_identical(gpu_lib, out_dtype):
+    xb = syn.activation_with_outliers(300, 640, seed=72)      # ragged M
+    wb = syn.gaussian((384, 640), seed=73, std=0.02)            # W [N][K]
+    x = dev(xb)
+    xq, xs, _ = gpu_lib.quant_act_1x128(x, "row")
+    q, s, q_t = gpu_lib.quant_weight_128x128(dev(wb), transposed=True)
+    qt, st, qt_t = gpu_lib.quant_weight_128x128(dev(wb), transposed=True, tiled=True)
+    a = gpu_lib.block_gemm("fprop", xq, xs, q, s, out_dtype=out_dtype)
+    b = gpu_lib.block_gemm("fprop_tiled", xq, xs, qt, st, out_dtype=out_dtype)
+    dyb = syn.gaussian((300, 384), seed=74, std=1e-3)            # dY [tokens][N]
+    dq, ds, _ = gpu_lib.quant_act_1x128(dev(dyb), "row")
+    c = gpu_lib.block_gemm("dgrad_t", dq, ds, q_t, s, out_dtype=out_dtype)
+    d = gpu_lib.block_gemm("dgrad_t_tiled", dq, ds, qt_t, st, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    view = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(a.view(view), b.view(view))
+    assert torch.equal(c.view(view), d.view(view))
+
+
+def test_tiled_full_size_bit_identical(gpu_lib):
+    x = dev(syn.activation_with_outliers(4096, 7168, seed=0))
+    w = dev(syn.gaussian((18432, 7168), seed=1, std=0.02))
+    xq, xs, _ = gpu_lib.quant_act_1x128(x, "row")
+    q, s, q_t = gpu_lib.quant_weight_128x128(w, transposed=True)
+    a = gpu_lib.block_gemm("fprop", xq, xs, q, s)
+    del q
+    qt, st, qt_t = gpu_lib.quant_weight_128x128(w, transposed=True, tiled=True)
+    b = gpu_lib.block_gemm("fprop_tiled", xq, xs, qt, st)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    del a, b, qt
+    dq, ds, _ = gpu_lib.quant_act_1x128(dev(syn.gaussian((4096, 18432), seed=4, std=1e-3)), "row")
+    c = gpu_lib.block_gemm("dgrad_t", dq, ds, q_t, s)
+    d = gpu_lib.block_gemm("dgrad_t_tiled", dq, ds, qt_t, st)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), d.view(torch.int16))
+
+
+def test_tiled_grouped_bit_identical(gpu_lib):
+    counts = np.array([3, 0, 130, 1, 257, 0, 600, 64])
+    off = dev(syn.expert_offsets(counts).astype(np.int32))
+    x = dev(syn.activation_with_outliers(int(counts.sum()), 1024, seed=75))
+    xq, xs, _ = gpu_lib.quant_act_1x128(x, "row")
+    ws = [gpu_lib.quant_weight_128x128(dev(syn.gaussian((256, 1024), seed=80 + e, std=0.02)))
+          for e in range(8)]
+    wt = [gpu_lib.quant_weight_128x128(dev(syn.gaussian((256, 1024), seed=80 + e, std=0.02)), tiled=True)
+          for e in range(8)]
+    B = torch.stack([w[0] for w in ws]).contiguous()
+    Bt = torch.stack([w[0] for w in wt]).contiguous()
+    S = torch.stack([w[1] for w in ws]).contiguous()
+    for out_dtype, view in ((torch.bfloat16, torch.int16), (torch.float32, torch.int32)):
+        a = gpu_lib.block_gemm_grouped(off, xq, xs, B, S, out_dtype=out_dtype)
+        b = gpu_lib.block_gemm_grouped(off, xq, xs, Bt, S, tiled=True, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(view), b.view(view))

@@ -103,7 +103,7 @@ def gemm(lib, layout=0, M=256, N=256, K=512, a=A, lda=512, sa=S, ld_sa=256, b=B,
 
 
 def test_gemm_validation(lib):
-    assert gemm(lib, layout=4) == UNSUP
+    assert gemm(lib, layout=6) == UNSUP
     assert gemm(lib, layout=-1) == UNSUP
     assert gemm(lib, dt=5) == UNSUP
     assert gemm(lib, K=200, lda=256) == SHAPE
@@ -125,6 +125,12 @@ def test_gemm_validation(lib):
     assert gemm(lib, layout=3, ldb=256) == LD
     assert gemm(lib, layout=3, ld_sb=1) == LD
     assert gemm(lib, layout=3, ld_sb=2) in (DEVICE, OK)
+    # *_TILED: B holds dense tiles, so ldb must equal K
+    assert gemm(lib, layout=4, ldb=528) == LD
+    assert gemm(lib, layout=4, N=200, ldc=256) == SHAPE
+    assert gemm(lib, layout=4) in (DEVICE, OK)
+    assert gemm(lib, layout=5, ldb=528, ld_sb=2) == LD
+    assert gemm(lib, layout=5, ld_sb=2) in (DEVICE, OK)
     # WGRAD: any N, column scales [K/128][N]
     assert gemm(lib, layout=2, N=200, ldc=208, ld_sb=150) == LD
     assert gemm(lib, layout=2, N=200, ldc=208, ld_sb=200, dt=1) in (DEVICE, OK)
@@ -237,6 +243,26 @@ def test_gemm_promotion_validation(lib):
     assert f(C_=A + 1024) == ALIAS
     for pk in (32, 64, 128, 384, 1 << 20):
         assert f(pk=pk) in (DEVICE, OK)
+
+
+def test_tiled_weight_and_grouped_validation(lib):
+    f = lambda w=X, rows=256, cols=512, ldw=512, q=Q, qt=None, s=S, lds=4: \
+        lib.fp8_quant_weight_128x128_tiled(w, rows, cols, ldw, q, qt, s, lds, None)
+    assert f(rows=200) == SHAPE
+    assert f(q=None) == NULL
+    assert f(ldw=256) == LD
+    assert f(lds=2) == LD
+    assert f(q=Q + 8) == ALIGN
+    assert f(q=X + 256) == ALIAS
+    assert f(qt=Q + 4096) == ALIAS                  # q_t overlaps the dense 256*512 q
+    assert f(qt=A) in (DEVICE, OK)
+    g = lib.fp8_block_gemm_grouped_tiled
+    args = [8, X, 1024, 256, 512, A, 512, S, 1024, B, S2, C, 0, 256, None]
+    assert g(*args) in (DEVICE, OK)
+    bad = list(args); bad[3] = 200
+    assert g(*bad) == SHAPE
+    bad = list(args); bad[0] = 0
+    assert g(*bad) == SHAPE
 
 
 def test_grouped_validation(lib):

@@ -12,7 +12,7 @@ seeded synthetic inputs already resident in HBM:
              (1x128 rows for Dgrad, 128x1 columns for Wgrad); Dgrad dX = dY W
              from the transposed weight codes W_q^T; 128x1 quantization of X +
              Wgrad dW = dY^T X (FP32 out).  Dgrad reads operand-tiled W_q^T
-             (also timed row-major).  Also reported: Dgrad reading W_q
+             and Wgrad operand-tiled X_q^T (both also timed row-major).  Also reported: Dgrad reading W_q
              as stored ("dgrad_lds") and the dY quantization as two separate
              passes ("dual_quant")
   grouped    1x128 quantization of X 16384x7168 + one grouped launch over 8
@@ -235,17 +235,20 @@ def main():
             dq, ds, dqt, dst = tm.region("bwd.quant_dual", lambda: fp8.quant_act_dual(d["dy4"]))
             tm.region("dgrad.gemm", lambda: fp8.block_gemm("dgrad_t_tiled", dq, ds, d["wq3t_tl"], d["ws3"]))
             tm.region("dgrad_lds.gemm", lambda: fp8.block_gemm("dgrad", dq, ds, d["wq3"], d["ws3"]))
-            xqt, xst, _ = tm.region("wgrad.quant_x", lambda: fp8.quant_act_1x128(d["x3"], "col"))
-            tm.region("wgrad.gemm", lambda: fp8.block_gemm("wgrad", dqt, dst, xqt, xst,
+            xqt, xst, _ = tm.region("wgrad.quant_x", lambda: fp8.quant_act_1x128(d["x3"], "col_tiled"))
+            tm.region("wgrad.gemm", lambda: fp8.block_gemm("wgrad_tiled", dqt, dst, xqt, xst,
                                                            out_dtype=torch.float32))
             ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
             tm.pending.append(("backward", ev0, ev1))
             tm.region("dgrad_rowmajor.gemm", lambda: fp8.block_gemm("dgrad_t", dq, ds, d["wq3t"], d["ws3"]))
+            xqr, xsr, _ = fp8.quant_act_1x128(d["x3"], "col")
+            tm.region("wgrad_rowmajor.gemm", lambda: fp8.block_gemm("wgrad", dqt, dst, xqr, xsr,
+                                                                    out_dtype=torch.float32))
             # the same two quantizations as separate passes, for comparison
             tm.region("bwd.quant_row", lambda: fp8.quant_act_1x128(d["dy4"], "row"))
             tm.region("bwd.quant_col", lambda: fp8.quant_act_1x128(d["dy4"], "col"))
             # X in both orientations from one read (Fprop rows, saved columns for Wgrad)
-            tm.region("fwd.quant_dual_x", lambda: fp8.quant_act_dual(d["x3"]))
+            tm.region("fwd.quant_dual_x", lambda: fp8.quant_act_dual(d["x3"], tiled=True))
             tm.region("fwd.quant_row_x", lambda: fp8.quant_act_1x128(d["x3"], "row"))
         if want("grouped"):
             ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
@@ -373,8 +376,11 @@ def main():
                          "ms_gemm_rowmajor_weights": tdr, "TFLOP/s_gemm_rowmajor_weights": F3 / tdr / 1e9}
         tl = tm.mean_ms("dgrad_lds.gemm")
         rows["dgrad_lds"] = {"ms_gemm": tl, "TFLOP/s_gemm": F3 / tl / 1e9, "layout": "dgrad (W_q read transposed)"}
+        twr = tm.mean_ms("wgrad_rowmajor.gemm")
         rows["wgrad"] = {"ms_quant_dy_share": tq2, "ms_quant_x_col": tq3, "ms_gemm": tg2,
                          "TFLOP/s_incl_quant": F3 / (tq2 + tq3 + tg2) / 1e9, "TFLOP/s_gemm": F3 / tg2 / 1e9,
+                         "layout": "wgrad_tiled (X_q^T operand-tiled)",
+                         "ms_gemm_rowmajor": twr, "TFLOP/s_gemm_rowmajor": F3 / twr / 1e9,
                          "col_quant_x_GB/s": 4096 * 7168 * (3 + 4 / 128) / tq3 / 1e6}
     if want("grouped"):
         F5 = 2.0 * 16384 * 2048 * 7168

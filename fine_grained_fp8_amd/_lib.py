@@ -16,8 +16,8 @@ STATUS = {
     0: "FP8_OK", 1: "FP8_ERR_NULL", 2: "FP8_ERR_SHAPE", 3: "FP8_ERR_LD", 4: "FP8_ERR_ALIGN",
     5: "FP8_ERR_UNSUPPORTED", 6: "FP8_ERR_DEVICE", 7: "FP8_ERR_LAUNCH", 8: "FP8_ERR_ALIAS",
 }
-TILE_ROW, TILE_COL = 0, 1
-LAYOUT = {"fprop": 0, "dgrad": 1, "wgrad": 2, "dgrad_t": 3, "fprop_tiled": 4, "dgrad_t_tiled": 5}
+TILE_ROW, TILE_COL, TILE_COL_TILED = 0, 1, 2
+LAYOUT = {"fprop": 0, "dgrad": 1, "wgrad": 2, "dgrad_t": 3, "fprop_tiled": 4, "dgrad_t_tiled": 5, "wgrad_tiled": 6}
 OUT_BF16, OUT_FP32 = 0, 1
 
 # name -> (restype, argtypes); mirrors include/fp8bs.h
@@ -30,6 +30,8 @@ SIGNATURES = {
                                            _P, _P, _P, _P]),
     "fp8_quant_act_dual": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
                                           _P]),
+    "fp8_quant_act_dual_tiled": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _I64,
+                                                _P]),
     "fp8_quant_weight_128x128": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
     "fp8_block_gemm": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P,
                                       _I64, _P, ctypes.c_int, _I64, _P]),

@@ -85,7 +85,15 @@ fp8_status fp8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_
                                fp8_tile_dir dir, uint8_t* q, int64_t ldq,
                                float* scales, int64_t ld_s, const float* scales_in,
                                float* amax_out, uint32_t* sat_count, void* stream) {
-  if (dir != FP8_TILE_ROW && dir != FP8_TILE_COL) return FP8_ERR_UNSUPPORTED;
+  if (dir != FP8_TILE_ROW && dir != FP8_TILE_COL && dir != FP8_TILE_COL_TILED)
+    return FP8_ERR_UNSUPPORTED;
+  const bool tiled = dir == FP8_TILE_COL_TILED;
+  if (tiled) {
+    // dense operand tiles of the transposed codes: [cols][rows], cols % 128
+    if (cols % 128 != 0) return FP8_ERR_SHAPE;
+    if (ldq != rows) return FP8_ERR_LD;
+    dir = FP8_TILE_COL;
+  }
   if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
   if (dir == FP8_TILE_ROW && cols % 128 != 0) return FP8_ERR_SHAPE;
   if (dir == FP8_TILE_COL && rows % 128 != 0) return FP8_ERR_SHAPE;
@@ -120,13 +128,13 @@ fp8_status fp8_quant_act_1x128(const void* x, int64_t rows, int64_t cols, int64_
   if (dir == FP8_TILE_ROW)
     return launched(fp8bs::launch_quant_rows(xb, rows, cols, ldx, q, ldq, scales_in ? nullptr : scales,
                                              ld_s, scales_in, amax_out, sat_count, st));
-  return launched(fp8bs::launch_quant_cols(xb, rows, cols, ldx, q, ldq, scales, ld_s, amax_out, st));
+  return launched(fp8bs::launch_quant_cols(xb, rows, cols, ldx, q, ldq, scales, ld_s, amax_out, tiled, st));
 }
 
-fp8_status fp8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx,
-                              uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t ld_s_row,
-                              uint8_t* q_col, int64_t ldq_col, float* s_col, int64_t ld_s_col,
-                              void* stream) {
+namespace {
+fp8_status quant_dual_impl(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* q_row,
+                           int64_t ldq_row, float* s_row, int64_t ld_s_row, uint8_t* q_col,
+                           int64_t ldq_col, float* s_col, int64_t ld_s_col, bool tiled, void* stream) {
   if (rows < 0 || cols < 0 || rows % 128 != 0 || cols % 128 != 0) return FP8_ERR_SHAPE;
   if (rows == 0 || cols == 0) return FP8_OK;
   if (!x || !q_row || !s_row || !q_col || !s_col) return FP8_ERR_NULL;
@@ -150,7 +158,24 @@ fp8_status fp8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t
   if (dev != FP8_OK) return dev;
   return launched(fp8bs::launch_quant_dual(static_cast<const uint16_t*>(x), rows, cols, ldx, q_row,
                                            ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col, ld_s_col,
-                                           reinterpret_cast<hipStream_t>(stream)));
+                                           tiled, reinterpret_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+fp8_status fp8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                              uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t ld_s_row,
+                              uint8_t* q_col, int64_t ldq_col, float* s_col, int64_t ld_s_col,
+                              void* stream) {
+  return quant_dual_impl(x, rows, cols, ldx, q_row, ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col,
+                         ld_s_col, false, stream);
+}
+
+fp8_status fp8_quant_act_dual_tiled(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                    uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t ld_s_row,
+                                    uint8_t* q_col_tiled, float* s_col, int64_t ld_s_col,
+                                    void* stream) {
+  return quant_dual_impl(x, rows, cols, ldx, q_row, ldq_row, s_row, ld_s_row, q_col_tiled, rows, s_col,
+                         ld_s_col, true, stream);
 }
 
 fp8_status fp8_pack_tokens(const void* x, int64_t x_rows, int64_t H, int64_t ldx,
@@ -318,10 +343,14 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
                           void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream) {
   if (layout != FP8_LAYOUT_FPROP && layout != FP8_LAYOUT_DGRAD && layout != FP8_LAYOUT_WGRAD &&
       layout != FP8_LAYOUT_DGRAD_T && layout != FP8_LAYOUT_FPROP_TILED &&
-      layout != FP8_LAYOUT_DGRAD_T_TILED)
+      layout != FP8_LAYOUT_DGRAD_T_TILED && layout != FP8_LAYOUT_WGRAD_TILED)
     return FP8_ERR_UNSUPPORTED;
-  const bool tiled = layout == FP8_LAYOUT_FPROP_TILED || layout == FP8_LAYOUT_DGRAD_T_TILED;
-  if (tiled) layout = layout == FP8_LAYOUT_FPROP_TILED ? FP8_LAYOUT_FPROP : FP8_LAYOUT_DGRAD_T;
+  const bool tiled = layout == FP8_LAYOUT_FPROP_TILED || layout == FP8_LAYOUT_DGRAD_T_TILED ||
+                     layout == FP8_LAYOUT_WGRAD_TILED;
+  if (tiled && N % 128 != 0) return FP8_ERR_SHAPE;
+  if (layout == FP8_LAYOUT_FPROP_TILED) layout = FP8_LAYOUT_FPROP;
+  if (layout == FP8_LAYOUT_DGRAD_T_TILED) layout = FP8_LAYOUT_DGRAD_T;
+  if (layout == FP8_LAYOUT_WGRAD_TILED) layout = FP8_LAYOUT_WGRAD;
   fp8_status st = validate_gemm_common(M, N, K, A, lda, sA, ld_sa, B, sB, C, c_dtype, ldc);
   if (st != FP8_OK || M == 0) return st;
   if (layout != FP8_LAYOUT_WGRAD && N % 128 != 0) return FP8_ERR_SHAPE;

@@ -706,7 +706,7 @@ hipError_t launch_typed(const GemmProblem& p, hipStream_t stream, int64_t grid, 
       hipLaunchKernelGGL((block_gemm_kernel<kLayout, false, kGrouped>), dim3((unsigned)grid),
                          dim3(kThreads), 0, stream, p, total);
     }
-  } else if constexpr (kLayout != kWgrad) {
+  } else {
     if (p.b_tiled) {
       if (p.out_fp32) {
         hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped, true>), dim3((unsigned)grid),
@@ -723,14 +723,6 @@ hipError_t launch_typed(const GemmProblem& p, hipStream_t stream, int64_t grid, 
         hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped, false>), dim3((unsigned)grid),
                            dim3(kThreads), 0, stream, p, total);
       }
-    }
-  } else {
-    if (p.out_fp32) {
-      hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped, false>), dim3((unsigned)grid),
-                         dim3(kThreads), 0, stream, p, total);
-    } else {
-      hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped, false>), dim3((unsigned)grid),
-                         dim3(kThreads), 0, stream, p, total);
     }
   }
   return hipGetLastError();

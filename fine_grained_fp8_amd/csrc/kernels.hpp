@@ -15,12 +15,12 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
 
 hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
-                             float* amax_out, hipStream_t stream);
+                             float* amax_out, bool tiled, hipStream_t stream);
 
 hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t ld_s_row,
                              uint8_t* q_col, int64_t ldq_col, float* s_col, int64_t ld_s_col,
-                             hipStream_t stream);
+                             bool tiled, hipStream_t stream);
 
 hipError_t launch_quant_weight(const uint16_t* w, int64_t rows, int64_t cols, int64_t ldw,
                                uint8_t* q, int64_t ldq, uint8_t* q_t, int64_t ldq_t,

@@ -124,13 +124,27 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 // padding after every group) and its rows are rotated by 8*(g >> 1) words,
 // which puts the 64 lanes of a column read on 64 distinct banks.
 // ---------------------------------------------------------------------------
+// Byte offset of the 16 transposed codes of column `col`, tokens
+// 128 rb + 16 g .. + 15: row-major [cols][ldq], or operand-tiled (the
+// transposed matrix has rows = columns of x and nbr 128-wide token blocks;
+// these 16 codes fill one lane slot of its 2 KB tile).
+template <bool kTiled>
+__device__ __forceinline__ int64_t transposed_code_offset(int64_t col, int64_t rb, int g, int64_t ldq,
+                                                          int64_t nbr) {
+  if constexpr (kTiled)
+    return ((col >> 4) * nbr + rb) * 2048 + (g >> 2) * 1024 + (((g & 3) << 4) + (col & 15)) * 16;
+  else
+    return col * ldq + rb * 128 + 16 * g;
+}
+
 __device__ __forceinline__ int cols_tile_word(int row, int word) {
   const int g = row >> 4;
   return g * 544 + (row & 15) * 32 + ((word + 8 * (g >> 1)) & 31);
 }
 
+template <bool kTiled>
 __global__ __launch_bounds__(256) void quant_cols_kernel(
-    const uint16_t* __restrict__ x, int64_t cols, int64_t ldx, int64_t ncb,
+    const uint16_t* __restrict__ x, int64_t cols, int64_t ldx, int64_t ncb, int64_t nbr,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int64_t ld_s,
     float* __restrict__ amax_out) {
   __shared__ uint32_t tile[8 * 544];
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
     }
     const int64_t col = c0 + 2 * p + h;
     if (col < cols) {
-      *reinterpret_cast<uint4*>(q + col * ldq + r0 + 16 * g) = out;
+      *reinterpret_cast<uint4*>(q + transposed_code_offset<kTiled>(col, rb, g, ldq, nbr)) = out;
       if (g == 0) {
         scales[rb * ld_s + col] = s;
         if (amax_out) amax_out[rb * ld_s + col] = amax_value(tt);
@@ -211,8 +225,9 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
 // (non-temporal).  Every code and scale equals the one the separate row and
 // column quantizers produce.
 // ---------------------------------------------------------------------------
+template <bool kTiled>
 __global__ __launch_bounds__(256) void quant_dual_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, int64_t ncb,
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t ncb, int64_t nbr,
     uint8_t* __restrict__ q_row, int64_t ldq_row, float* __restrict__ s_row, int64_t ld_s_row,
     uint8_t* __restrict__ q_col, int64_t ldq_col, float* __restrict__ s_col, int64_t ld_s_col) {
   // BF16 pairs: word c of row r holds columns 2c, 2c+1 and sits at word
@@ -300,7 +315,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
       }
       const int64_t col = c0 + 2 * cp + h;
       __builtin_nontemporal_store(sv4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
-                                  reinterpret_cast<sv4i*>(q_col + col * ldq_col + r0 + 16 * g));
+                                  reinterpret_cast<sv4i*>(q_col + transposed_code_offset<kTiled>(col, rb, g, ldq_col, nbr)));
       if (g == 0) s_col[rb * ld_s_col + col] = s;
     }
   }
@@ -455,21 +470,31 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
 hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t ld_s_row,
                              uint8_t* q_col, int64_t ldq_col, float* s_col, int64_t ld_s_col,
-                             hipStream_t stream) {
+                             bool tiled, hipStream_t stream) {
   const int64_t ncb = cols / 128;
   const int64_t nblocks = (rows / 128) * ncb;
-  hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, x, ldx, ncb,
-                     q_row, ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col, ld_s_col);
+  const int64_t nbr = rows / 128;
+  if (tiled)
+    hipLaunchKernelGGL(quant_dual_kernel<true>, dim3((unsigned)nblocks), dim3(256), 0, stream, x, ldx, ncb,
+                       nbr, q_row, ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col, ld_s_col);
+  else
+    hipLaunchKernelGGL(quant_dual_kernel<false>, dim3((unsigned)nblocks), dim3(256), 0, stream, x, ldx, ncb,
+                       nbr, q_row, ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col, ld_s_col);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
-                             float* amax_out, hipStream_t stream) {
+                             float* amax_out, bool tiled, hipStream_t stream) {
   const int64_t ncb = (cols + 63) / 64;
   const int64_t nblocks = (rows / 128) * ncb;
-  hipLaunchKernelGGL(quant_cols_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream,
-                     x, cols, ldx, ncb, q, ldq, scales, ld_s, amax_out);
+  const int64_t nbr = rows / 128;
+  if (tiled)
+    hipLaunchKernelGGL(quant_cols_kernel<true>, dim3((unsigned)nblocks), dim3(256), 0, stream,
+                       x, cols, ldx, ncb, nbr, q, ldq, scales, ld_s, amax_out);
+  else
+    hipLaunchKernelGGL(quant_cols_kernel<false>, dim3((unsigned)nblocks), dim3(256), 0, stream,
+                       x, cols, ldx, ncb, nbr, q, ldq, scales, ld_s, amax_out);
   return hipGetLastError();
 }
 

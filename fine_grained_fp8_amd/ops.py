@@ -52,6 +52,8 @@ def quant_act_1x128(x: torch.Tensor, direction: str = "row", *, scales_in=None,
         q [rows][cols] uint8, scales [cols/128][round_up(rows, 4)] float32.
     direction "col": 128x1 tiles along each column, transposed output; returns
         q [cols][rows] uint8, scales [rows/128][round_up(cols, 4)] float32.
+    direction "col_tiled": as "col" with q holding the operand-tiled bytes of
+        the transposed codes (for the "wgrad_tiled" GEMM layout).
     scales_in (row only): caller scales in the scale layout; then the returned
     scales are None.  return_amax adds the per-tile max |x| (same layout).
     sat_count: optional int32/uint32 device tensor of one element, incremented.
@@ -65,10 +67,10 @@ def quant_act_1x128(x: torch.Tensor, direction: str = "row", *, scales_in=None,
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
         s_shape = (cols // 128, round_up(rows, 4))
         tile_dir = _lib.TILE_ROW
-    elif direction == "col":
+    elif direction in ("col", "col_tiled"):
         q = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
         s_shape = (rows // 128, round_up(cols, 4))
-        tile_dir = _lib.TILE_COL
+        tile_dir = _lib.TILE_COL if direction == "col" else _lib.TILE_COL_TILED
     else:
         raise ValueError(direction)
     if scales_in is not None:
@@ -87,12 +89,12 @@ def quant_act_1x128(x: torch.Tensor, direction: str = "row", *, scales_in=None,
     return q, scales, amax
 
 
-def quant_act_dual(x: torch.Tensor, *, stream=None):
+def quant_act_dual(x: torch.Tensor, *, tiled: bool = False, stream=None):
     """Both orientations of x [rows][cols] BF16 from one read.
 
     Returns (q_row [rows][cols], s_row [cols/128][round_up(rows, 4)],
              q_col [cols][rows], s_col [rows/128][round_up(cols, 4)]) - the outputs of
-    quant_act_1x128(x, "row") and quant_act_1x128(x, "col").
+    quant_act_1x128(x, "row") and quant_act_1x128(x, "col") ("col_tiled" if tiled).
     """
     lib = _lib.load_library()
     _check_2d("x", x, _BF16)
@@ -101,6 +103,12 @@ def quant_act_dual(x: torch.Tensor, *, stream=None):
     s_row = torch.empty((cols // 128, round_up(rows, 4)), dtype=torch.float32, device=x.device)
     q_col = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
     s_col = torch.empty((rows // 128, round_up(cols, 4)), dtype=torch.float32, device=x.device)
+    if tiled:
+        st = lib.fp8_quant_act_dual_tiled(_ptr(x), rows, cols, x.stride(0), _ptr(q_row), q_row.stride(0),
+                                          _ptr(s_row), s_row.stride(0), _ptr(q_col), _ptr(s_col),
+                                          s_col.stride(0), _stream(stream))
+        _lib.check("fp8_quant_act_dual_tiled", st)
+        return q_row, s_row, q_col, s_col
     st = lib.fp8_quant_act_dual(_ptr(x), rows, cols, x.stride(0), _ptr(q_row), q_row.stride(0),
                                 _ptr(s_row), s_row.stride(0), _ptr(q_col), q_col.stride(0),
                                 _ptr(s_col), s_col.stride(0), _stream(stream))
@@ -143,8 +151,10 @@ def block_gemm(layout: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, 
     dgrad_t: A [M][K], sA [K/128][>=M], B [N][K] (W_q^T, the q_t of the weight
              quantizer), sB [K/128][>=N/128] (the forward block-scale table)
     wgrad: A [M][K], sA [K/128][>=M], B [N][K], sB [K/128][>=N]
-    fprop_tiled / dgrad_t_tiled: as fprop / dgrad_t with B holding the
-             operand-tiled bytes (quant_weight_128x128(..., tiled=True))
+    fprop_tiled / dgrad_t_tiled / wgrad_tiled: as fprop / dgrad_t / wgrad with
+             B holding the operand-tiled bytes (quant_weight_128x128(...,
+             tiled=True); for wgrad quant_act_1x128(x, "col_tiled") or
+             quant_act_dual(x, tiled=True))
     Returns C [M][N] in out_dtype (bfloat16 or float32).
     """
     lib = _lib.load_library()

@@ -78,7 +78,8 @@ typedef enum {
 
 typedef enum {
   FP8_TILE_ROW = 0, /* 1x128 tiles along the columns of each row */
-  FP8_TILE_COL = 1  /* 128x1 tiles along the rows of each column; output transposed */
+  FP8_TILE_COL = 1, /* 128x1 tiles along the rows of each column; output transposed */
+  FP8_TILE_COL_TILED = 2 /* FP8_TILE_COL with the transposed codes written operand-tiled */
 } fp8_tile_dir;
 
 typedef enum {
@@ -87,7 +88,8 @@ typedef enum {
   FP8_LAYOUT_WGRAD = 2, /* C[M][N] = A[M][K] . B[N][K]^T,  K = tokens, per-row x per-column scales */
   FP8_LAYOUT_DGRAD_T = 3, /* C[M][N] = A[M][K] . B[N][K]^T,  B = W_q^T (transposed weight codes) */
   FP8_LAYOUT_FPROP_TILED = 4,  /* FPROP with B in the operand-tiled layout (ldb == K) */
-  FP8_LAYOUT_DGRAD_T_TILED = 5 /* DGRAD_T with B in the operand-tiled layout (ldb == K) */
+  FP8_LAYOUT_DGRAD_T_TILED = 5, /* DGRAD_T with B in the operand-tiled layout (ldb == K) */
+  FP8_LAYOUT_WGRAD_TILED = 6    /* WGRAD with B = X_q^T in the operand-tiled layout (ldb == K) */
 } fp8_gemm_layout;
 
 typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_FP32 = 1 } fp8_out_dtype;
@@ -104,6 +106,9 @@ typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_FP32 = 1 } fp8_out_dtype;
  *                                                     GEMM's A-scale layout
  *             FP8_TILE_COL: tiles of 128x1 along each column (weight-gradient
  *             operands, tiles along tokens); requires rows % 128 == 0.
+ *             FP8_TILE_COL_TILED: the same codes written in the operand-tiled
+ *             layout of fp8_quant_weight_128x128_tiled (R = cols, C = rows),
+ *             for FP8_LAYOUT_WGRAD_TILED; also cols % 128 == 0 and ldq == rows.
  *               q      [cols][ldq >= rows]            transposed codes (K-contiguous
  *                                                     for the Wgrad GEMM)
  *               scales [rows/128][ld_s >= cols]       FP32
@@ -146,6 +151,13 @@ fp8_status fp8_quant_act_dual(const void* x, int64_t rows, int64_t cols, int64_t
                               uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t ld_s_row,
                               uint8_t* q_col, int64_t ldq_col, float* s_col, int64_t ld_s_col,
                               void* stream);
+
+/* fp8_quant_act_dual_tiled - fp8_quant_act_dual with the column-tile codes
+ * written operand-tiled (dense, cols * rows bytes; see FP8_TILE_COL_TILED). */
+fp8_status fp8_quant_act_dual_tiled(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                    uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t ld_s_row,
+                                    uint8_t* q_col_tiled, float* s_col, int64_t ld_s_col,
+                                    void* stream);
 
 /*
  * fp8_quant_weight_128x128 - 128x128 weight-block quantization, blocks
@@ -204,10 +216,12 @@ fp8_status fp8_quant_weight_128x128_tiled(const void* w, int64_t rows, int64_t c
  *  FP8_LAYOUT_WGRAD   (M = d_out, N = d_in, K = tokens)
  *     A  = dY_q^T [M][lda >= K];   sA [K/128][ld_sa >= M]     (128x1 column scales)
  *     B  = X_q^T  [N][ldb >= K];   sB [K/128][ld_sb >= N]     (128x1 column scales)
- *  FP8_LAYOUT_FPROP_TILED, FP8_LAYOUT_DGRAD_T_TILED - FPROP and DGRAD_T with B
- *     in the operand-tiled layout of fp8_quant_weight_128x128_tiled (q_tiled,
- *     resp. q_t_tiled); ldb must equal K.  Bit-identical results; the weight
- *     loads become whole contiguous lines.
+ *  FP8_LAYOUT_FPROP_TILED, FP8_LAYOUT_DGRAD_T_TILED, FP8_LAYOUT_WGRAD_TILED -
+ *     FPROP, DGRAD_T and WGRAD with B in the operand-tiled layout
+ *     (fp8_quant_weight_128x128_tiled's q_tiled / q_t_tiled; for WGRAD the
+ *     FP8_TILE_COL_TILED or fp8_quant_act_dual_tiled codes of X); ldb must
+ *     equal K and N % 128 == 0.  Bit-identical results; the B-side loads
+ *     become whole contiguous lines.
  *  C: [M][ldc >= N], BF16 (round to nearest even) or FP32 (c_dtype).
  *  M == 0 is a no-op.  C must not overlap A, B or the scales.
  */

@@ -328,3 +328,40 @@ def test_tiled_grouped_bit_identical(gpu_lib):
         b = gpu_lib.block_gemm_grouped(off, xq, xs, Bt, S, tiled=True, out_dtype=out_dtype)
         torch.cuda.synchronize()
         assert torch.equal(a.view(view), b.view(view))
+
+
+def test_tiled_column_codes_and_wgrad(gpu_lib):
+    """128x1 column codes written operand-tiled (column quantizer and dual
+    pass) match the oracle's layout, and Wgrad reading them is bit-identical
+    to Wgrad on the row-major codes."""
+    from oracle import tiling
+    xb = syn.activation_with_outliers(384, 640, seed=91)        # X [tokens][d_in]
+    dyb = syn.gaussian((384, 256), seed=92, std=1e-3)            # dY [tokens][d_out]
+    x, dy = dev(xb), dev(dyb)
+    qx, sx, _ = gpu_lib.quant_act_1x128(x, "col")
+    qx_t, sx_t, _ = gpu_lib.quant_act_1x128(x, "col_tiled")
+    qo, _ = quant.quant_cols(xb)
+    assert np.array_equal(qx_t.cpu().numpy().ravel(), tiling.tile_codes(qo))
+    assert torch.equal(sx, sx_t)
+    r0, s0, c0, t0 = gpu_lib.quant_act_dual(x)
+    r1, s1, c1, t1 = gpu_lib.quant_act_dual(x, tiled=True)
+    assert torch.equal(r0, r1) and torch.equal(s0, s1) and torch.equal(t0, t1)
+    assert torch.equal(c1, qx_t)
+    qd, sd, _ = gpu_lib.quant_act_1x128(dy, "col")
+    for out_dtype, view in ((torch.float32, torch.int32), (torch.bfloat16, torch.int16)):
+        a = gpu_lib.block_gemm("wgrad", qd, sd, qx, sx, out_dtype=out_dtype)
+        b = gpu_lib.block_gemm("wgrad_tiled", qd, sd, qx_t, sx_t, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(view), b.view(view))
+
+
+def test_tiled_wgrad_full_size_bit_identical(gpu_lib):
+    x = dev(syn.activation_with_outliers(4096, 7168, seed=0))
+    dy = dev(syn.gaussian((4096, 18432), seed=4, std=1e-3))
+    _, _, qd, sd = gpu_lib.quant_act_dual(dy)
+    _, _, qx, sx = gpu_lib.quant_act_dual(x)
+    _, _, qx_t, sx_t = gpu_lib.quant_act_dual(x, tiled=True)
+    a = gpu_lib.block_gemm("wgrad", qd, sd, qx, sx, out_dtype=torch.float32)
+    b = gpu_lib.block_gemm("wgrad_tiled", qd, sd, qx_t, sx_t, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))

@@ -103,7 +103,7 @@ def gemm(lib, layout=0, M=256, N=256, K=512, a=A, lda=512, sa=S, ld_sa=256, b=B,
 
 
 def test_gemm_validation(lib):
-    assert gemm(lib, layout=6) == UNSUP
+    assert gemm(lib, layout=7) == UNSUP
     assert gemm(lib, layout=-1) == UNSUP
     assert gemm(lib, dt=5) == UNSUP
     assert gemm(lib, K=200, lda=256) == SHAPE
@@ -131,6 +131,9 @@ def test_gemm_validation(lib):
     assert gemm(lib, layout=4) in (DEVICE, OK)
     assert gemm(lib, layout=5, ldb=528, ld_sb=2) == LD
     assert gemm(lib, layout=5, ld_sb=2) in (DEVICE, OK)
+    assert gemm(lib, layout=6, N=200, ldc=208, ld_sb=200, dt=1) == SHAPE   # tiled B: N % 128
+    assert gemm(lib, layout=6, ldb=528, ld_sb=256, dt=1) == LD
+    assert gemm(lib, layout=6, ld_sb=256, dt=1) in (DEVICE, OK)
     # WGRAD: any N, column scales [K/128][N]
     assert gemm(lib, layout=2, N=200, ldc=208, ld_sb=150) == LD
     assert gemm(lib, layout=2, N=200, ldc=208, ld_sb=200, dt=1) in (DEVICE, OK)
@@ -243,6 +246,19 @@ def test_gemm_promotion_validation(lib):
     assert f(C_=A + 1024) == ALIAS
     for pk in (32, 64, 128, 384, 1 << 20):
         assert f(pk=pk) in (DEVICE, OK)
+
+
+def test_tiled_column_codes_validation(lib):
+    f = lambda x=X, rows=256, cols=384, ldx=384, d=2, q=Q, ldq=256, s=S, lds=384: \
+        lib.fp8_quant_act_1x128(x, rows, cols, ldx, d, q, ldq, s, lds, None, None, None, None)
+    assert f() in (DEVICE, OK)
+    assert f(cols=200, ldx=208, lds=208) == SHAPE       # tiled: cols % 128
+    assert f(ldq=272) == LD                              # dense: ldq == rows
+    assert f(d=1, cols=200, ldx=208, lds=208) in (DEVICE, OK)   # the row-major COL keeps ragged cols
+    g = lambda qc=B, sc=S2: lib.fp8_quant_act_dual_tiled(X, 256, 384, 384, A, 384, S, 256, qc, sc, 384, None)
+    assert g() in (DEVICE, OK)
+    assert g(qc=None) == NULL
+    assert g(qc=A + 1024) == ALIAS
 
 
 def test_tiled_weight_and_grouped_validation(lib):

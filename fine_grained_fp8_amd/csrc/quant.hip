@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
 // ---------------------------------------------------------------------------
 template <bool kTiled>
 __global__ __launch_bounds__(256) void quant_dual_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, int64_t ncb, int64_t nbr,
+    const uint16_t* __restrict__ x, int64_t ldx, int64_t ncb, int64_t nbr, int64_t nblocks,
     uint8_t* __restrict__ q_row, int64_t ldq_row, float* __restrict__ s_row, int64_t ld_s_row,
     uint8_t* __restrict__ q_col, int64_t ldq_col, float* __restrict__ s_col, int64_t ld_s_col) {
   // BF16 pairs: word c of row r holds columns 2c, 2c+1 and sits at word
@@ -236,88 +236,104 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int sub = lane >> 4, l16 = lane & 15;
-  const int64_t rb = blockIdx.x / ncb;
-  const int64_t kb = blockIdx.x % ncb;
-  const int64_t r0 = rb * 128, c0 = kb * 128;
 
   // ---- load: row wave*32 + 4i + sub, 8 BF16 at columns 8*l16.. ----
   uint4 v[8];
+  auto load_block = [&](int64_t blk) {
+    const int64_t r0 = (blk / ncb) * 128, c0 = (blk % ncb) * 128;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = wave * 32 + 4 * i + sub;
-    const sv4i u = __builtin_nontemporal_load(reinterpret_cast<const sv4i*>(x + (r0 + row) * ldx + c0 + l16 * 8));
-    v[i] = make_uint4((uint32_t)u.x, (uint32_t)u.y, (uint32_t)u.z, (uint32_t)u.w);
-    *reinterpret_cast<uint4*>(&tile[row][(l16 * 4) ^ (8 * ((row >> 4) & 7))]) = v[i];
-  }
-
-  // ---- 1x128 row tiles, from registers ----
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = wave * 32 + 4 * i + sub;
-    const uint32_t ta = row16_max_u32(absmax_bits8(v[i]));
-    const float s = tile_scale(ta);
-    const uint4 d = v[i];
-    uint2 out;
-    if (ta < kBf16InfAbs) {
-      const float r = 1.0f / s;
-      out.x = pack4_sat(div_by_scale(bf16_lo(d.x), s, r), div_by_scale(bf16_hi(d.x), s, r),
-                        div_by_scale(bf16_lo(d.y), s, r), div_by_scale(bf16_hi(d.y), s, r));
-      out.y = pack4_sat(div_by_scale(bf16_lo(d.z), s, r), div_by_scale(bf16_hi(d.z), s, r),
-                        div_by_scale(bf16_lo(d.w), s, r), div_by_scale(bf16_hi(d.w), s, r));
-    } else {
-      out.x = pack4_sat_nan(bf16_lo(d.x) / s, bf16_hi(d.x) / s, bf16_lo(d.y) / s, bf16_hi(d.y) / s);
-      out.y = pack4_sat_nan(bf16_lo(d.z) / s, bf16_hi(d.z) / s, bf16_lo(d.w) / s, bf16_hi(d.w) / s);
+    for (int i = 0; i < 8; ++i) {
+      const int row = wave * 32 + 4 * i + sub;
+      const sv4i u = __builtin_nontemporal_load(reinterpret_cast<const sv4i*>(x + (r0 + row) * ldx + c0 + l16 * 8));
+      v[i] = make_uint4((uint32_t)u.x, (uint32_t)u.y, (uint32_t)u.z, (uint32_t)u.w);
     }
-    __builtin_nontemporal_store(sv2i{(int)out.x, (int)out.y},
-                                reinterpret_cast<sv2i*>(q_row + (r0 + row) * ldq_row + c0 + l16 * 8));
-    if (l16 == 0) s_row[kb * ld_s_row + r0 + row] = s;
-  }
-  __syncthreads();
-
-  // ---- 128x1 column tiles, from LDS ----
-  // Lane 8j + g of wave w takes column pair cp = 32*pass + 8w + j and rows
-  // 16g..16g+15; the 8 lanes of a pair reduce its amax with DPP and then
-  // write each column's 128 codes as one contiguous 128-byte run.
-  const int g = lane & 7, j = lane >> 3;
+  };
+  // A workgroup takes blocks blockIdx.x, blockIdx.x + gridDim.x, ...: the
+  // next block's loads are issued as soon as the row tiles have used the
+  // registers, so they are in flight during the column phase.
+  int64_t blk = blockIdx.x;
+  if (blk < nblocks) load_block(blk);
+  for (; blk < nblocks; blk += gridDim.x) {
+    const int64_t rb = blk / ncb;
+    const int64_t kb = blk % ncb;
+    const int64_t r0 = rb * 128, c0 = kb * 128;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int cp = 32 * pass + 8 * wave + j;
-    uint32_t d[16];
-    us2 m = {0, 0};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      d[i] = tile[16 * g + i][cp ^ (8 * g)];
-      m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[i] & 0x7FFF7FFFu));
+    for (int i = 0; i < 8; ++i) {
+      const int row = wave * 32 + 4 * i + sub;
+      *reinterpret_cast<uint4*>(&tile[row][(l16 * 4) ^ (8 * ((row >> 4) & 7))]) = v[i];
     }
-    const uint32_t mm = row8_max_pk_u16(__builtin_bit_cast(uint32_t, m));
+
+    // ---- 1x128 row tiles, from registers ----
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t tt = h ? (mm >> 16) : (mm & 0xFFFFu);
-      const float s = tile_scale(tt);
-      uint32_t w[4];
-      if (tt < kBf16InfAbs) {
+    for (int i = 0; i < 8; ++i) {
+      const int row = wave * 32 + 4 * i + sub;
+      const uint32_t ta = row16_max_u32(absmax_bits8(v[i]));
+      const float s = tile_scale(ta);
+      const uint4 d = v[i];
+      uint2 out;
+      if (ta < kBf16InfAbs) {
         const float r = 1.0f / s;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = div_by_scale(h ? bf16_hi(d[4 * k + e]) : bf16_lo(d[4 * k + e]), s, r);
-          w[k] = pack4_sat(y[0], y[1], y[2], y[3]);
-        }
+        out.x = pack4_sat(div_by_scale(bf16_lo(d.x), s, r), div_by_scale(bf16_hi(d.x), s, r),
+                          div_by_scale(bf16_lo(d.y), s, r), div_by_scale(bf16_hi(d.y), s, r));
+        out.y = pack4_sat(div_by_scale(bf16_lo(d.z), s, r), div_by_scale(bf16_hi(d.z), s, r),
+                          div_by_scale(bf16_lo(d.w), s, r), div_by_scale(bf16_hi(d.w), s, r));
       } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = (h ? bf16_hi(d[4 * k + e]) : bf16_lo(d[4 * k + e])) / s;
-          w[k] = pack4_sat_nan(y[0], y[1], y[2], y[3]);
-        }
+        out.x = pack4_sat_nan(bf16_lo(d.x) / s, bf16_hi(d.x) / s, bf16_lo(d.y) / s, bf16_hi(d.y) / s);
+        out.y = pack4_sat_nan(bf16_lo(d.z) / s, bf16_hi(d.z) / s, bf16_lo(d.w) / s, bf16_hi(d.w) / s);
       }
-      const int64_t col = c0 + 2 * cp + h;
-      __builtin_nontemporal_store(sv4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
-                                  reinterpret_cast<sv4i*>(q_col + transposed_code_offset<kTiled>(col, rb, g, ldq_col, nbr)));
-      if (g == 0) s_col[rb * ld_s_col + col] = s;
+      __builtin_nontemporal_store(sv2i{(int)out.x, (int)out.y},
+                                  reinterpret_cast<sv2i*>(q_row + (r0 + row) * ldq_row + c0 + l16 * 8));
+      if (l16 == 0) s_row[kb * ld_s_row + r0 + row] = s;
     }
+    if (blk + gridDim.x < nblocks) load_block(blk + gridDim.x);
+    __syncthreads();
+
+    // ---- 128x1 column tiles, from LDS ----
+    // Lane 8j + g of wave w takes column pair cp = 32*pass + 8w + j and rows
+    // 16g..16g+15; the 8 lanes of a pair reduce its amax with DPP and then
+    // write each column's 128 codes as one contiguous 128-byte run.
+    const int g = lane & 7, j = lane >> 3;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int cp = 32 * pass + 8 * wave + j;
+      uint32_t d[16];
+      us2 m = {0, 0};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        d[i] = tile[16 * g + i][cp ^ (8 * g)];
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[i] & 0x7FFF7FFFu));
+      }
+      const uint32_t mm = row8_max_pk_u16(__builtin_bit_cast(uint32_t, m));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t tt = h ? (mm >> 16) : (mm & 0xFFFFu);
+        const float s = tile_scale(tt);
+        uint32_t w[4];
+        if (tt < kBf16InfAbs) {
+          const float r = 1.0f / s;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = div_by_scale(h ? bf16_hi(d[4 * k + e]) : bf16_lo(d[4 * k + e]), s, r);
+            w[k] = pack4_sat(y[0], y[1], y[2], y[3]);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = (h ? bf16_hi(d[4 * k + e]) : bf16_lo(d[4 * k + e])) / s;
+            w[k] = pack4_sat_nan(y[0], y[1], y[2], y[3]);
+          }
+        }
+        const int64_t col = c0 + 2 * cp + h;
+        __builtin_nontemporal_store(sv4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
+                                    reinterpret_cast<sv4i*>(q_col + transposed_code_offset<kTiled>(col, rb, g, ldq_col, nbr)));
+        if (g == 0) s_col[rb * ld_s_col + col] = s;
+      }
+    }
+    __syncthreads();   // the next block overwrites the tile
   }
 }
 
@@ -474,12 +490,13 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
   const int64_t ncb = cols / 128;
   const int64_t nblocks = (rows / 128) * ncb;
   const int64_t nbr = rows / 128;
+  const int64_t grid = (nblocks + 1) / 2;      // two blocks per workgroup
   if (tiled)
-    hipLaunchKernelGGL(quant_dual_kernel<true>, dim3((unsigned)nblocks), dim3(256), 0, stream, x, ldx, ncb,
-                       nbr, q_row, ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col, ld_s_col);
+    hipLaunchKernelGGL(quant_dual_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, x, ldx, ncb,
+                       nbr, nblocks, q_row, ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col, ld_s_col);
   else
-    hipLaunchKernelGGL(quant_dual_kernel<false>, dim3((unsigned)nblocks), dim3(256), 0, stream, x, ldx, ncb,
-                       nbr, q_row, ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col, ld_s_col);
+    hipLaunchKernelGGL(quant_dual_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, x, ldx, ncb,
+                       nbr, nblocks, q_row, ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col, ld_s_col);
   return hipGetLastError();
 }
 

@@ -137,6 +137,37 @@ __device__ __forceinline__ int64_t transposed_code_offset(int64_t col, int64_t r
     return col * ldq + rb * 128 + 16 * g;
 }
 
+// Operand-tiled store of a column pair's codes from lanes 8j + g (g = the
+// 16-token group, o0 / o1 = columns col0 / col0 + 1): adjacent lanes g, g^1
+// swap one value so that each store instruction covers 16 consecutive
+// columns of one token group - whole 256-byte runs of the tiles - instead of
+// every other 16-byte slot.
+__device__ __forceinline__ uint4 swap_adjacent(uint4 v) {
+  return make_uint4((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, 0xB1, 0xF, 0xF, true),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, 0xB1, 0xF, 0xF, true),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.z, 0xB1, 0xF, 0xF, true),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, 0xB1, 0xF, 0xF, true));
+}
+
+template <bool kNontemporal>
+__device__ __forceinline__ void store_pair_tiled(uint8_t* q, uint4 o0, uint4 o1, int64_t col0, int64_t rb,
+                                                 int g, int64_t nbr) {
+  const bool odd = g & 1;
+  const uint4 recv = swap_adjacent(odd ? o0 : o1);
+  const int64_t col = col0 + (odd ? 1 : 0);
+  const uint4 a = odd ? recv : o0;           // token group g & ~1
+  const uint4 b = odd ? o1 : recv;           // token group g | 1
+  uint8_t* pa = q + transposed_code_offset<true>(col, rb, g & ~1, 0, nbr);
+  uint8_t* pb = q + transposed_code_offset<true>(col, rb, g | 1, 0, nbr);
+  if constexpr (kNontemporal) {
+    __builtin_nontemporal_store(sv4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w}, reinterpret_cast<sv4i*>(pa));
+    __builtin_nontemporal_store(sv4i{(int)b.x, (int)b.y, (int)b.z, (int)b.w}, reinterpret_cast<sv4i*>(pb));
+  } else {
+    *reinterpret_cast<uint4*>(pa) = a;
+    *reinterpret_cast<uint4*>(pb) = b;
+  }
+}
+
 __device__ __forceinline__ int cols_tile_word(int row, int word) {
   const int g = row >> 4;
   return g * 544 + (row & 15) * 32 + ((word + 8 * (g >> 1)) & 31);
@@ -179,6 +210,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
     m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[i] & 0x7FFF7FFFu));
   }
   const uint32_t mm = row8_max_pk_u16(__builtin_bit_cast(uint32_t, m));
+  uint4 outs[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t tt = h ? (mm >> 16) : (mm & 0xFFFFu);
@@ -203,15 +235,18 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
       out.z = pack4_sat_nan(y[8], y[9], y[10], y[11]);
       out.w = pack4_sat_nan(y[12], y[13], y[14], y[15]);
     }
+    outs[h] = out;
     const int64_t col = c0 + 2 * p + h;
     if (col < cols) {
-      *reinterpret_cast<uint4*>(q + transposed_code_offset<kTiled>(col, rb, g, ldq, nbr)) = out;
+      if constexpr (!kTiled) *reinterpret_cast<uint4*>(q + transposed_code_offset<false>(col, rb, g, ldq, nbr)) = out;
       if (g == 0) {
         scales[rb * ld_s + col] = s;
         if (amax_out) amax_out[rb * ld_s + col] = amax_value(tt);
       }
     }
   }
+  // tiled output: cols % 128 == 0, so both columns exist
+  if constexpr (kTiled) store_pair_tiled<false>(q, outs[0], outs[1], c0 + 2 * p, rb, g, nbr);
 }
 
 // ---------------------------------------------------------------------------
@@ -304,6 +339,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
         m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[i] & 0x7FFF7FFFu));
       }
       const uint32_t mm = row8_max_pk_u16(__builtin_bit_cast(uint32_t, m));
+      uint4 outs[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t tt = h ? (mm >> 16) : (mm & 0xFFFFu);
@@ -328,10 +364,13 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
           }
         }
         const int64_t col = c0 + 2 * cp + h;
-        __builtin_nontemporal_store(sv4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
-                                    reinterpret_cast<sv4i*>(q_col + transposed_code_offset<kTiled>(col, rb, g, ldq_col, nbr)));
+        outs[h] = make_uint4(w[0], w[1], w[2], w[3]);
+        if constexpr (!kTiled)
+          __builtin_nontemporal_store(sv4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
+                                      reinterpret_cast<sv4i*>(q_col + transposed_code_offset<false>(col, rb, g, ldq_col, nbr)));
         if (g == 0) s_col[rb * ld_s_col + col] = s;
       }
+      if constexpr (kTiled) store_pair_tiled<true>(q_col, outs[0], outs[1], c0 + 2 * cp, rb, g, nbr);
     }
     __syncthreads();   // the next block overwrites the tile
   }

@@ -176,77 +176,95 @@ __device__ __forceinline__ int cols_tile_word(int row, int word) {
 template <bool kTiled>
 __global__ __launch_bounds__(256) void quant_cols_kernel(
     const uint16_t* __restrict__ x, int64_t cols, int64_t ldx, int64_t ncb, int64_t nbr,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int64_t ld_s,
-    float* __restrict__ amax_out) {
+    int64_t nblocks, uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales,
+    int64_t ld_s, float* __restrict__ amax_out) {
   __shared__ uint32_t tile[8 * 544];
   const int t = threadIdx.x;
-  const int64_t rb = blockIdx.x / ncb;
-  const int64_t c0 = (blockIdx.x % ncb) * 64;
-  const int64_t r0 = rb * 128;
+  uint4 vals[4];
+  auto load_block = [&](int64_t blk) {
+    const int64_t lr0 = (blk / ncb) * 128, lc0 = (blk % ncb) * 64;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ci = t + 256 * i;
-    const int row = ci >> 3, cc = ci & 7;
-    const int64_t col = c0 + cc * 8;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    const uint16_t* src = x + (r0 + row) * ldx + col;
-    if (col + 8 <= cols) {
-      val = *reinterpret_cast<const uint4*>(src);
-    } else if (col < cols) {                 // ragged last chunk: stay inside the row
-      uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int e = 0; e < 8 && col + e < cols; ++e) h[e] = src[e];
-      val = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    for (int i = 0; i < 4; ++i) {
+      const int ci = t + 256 * i;
+      const int row = ci >> 3, cc = ci & 7;
+      const int64_t col = lc0 + cc * 8;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      const uint16_t* src = x + (lr0 + row) * ldx + col;
+      if (col + 8 <= cols) {
+        val = *reinterpret_cast<const uint4*>(src);
+      } else if (col < cols) {               // ragged last chunk: stay inside the row
+        uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int e = 0; e < 8 && col + e < cols; ++e) h[e] = src[e];
+        val = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      }
+      vals[i] = val;
     }
-    *reinterpret_cast<uint4*>(&tile[cols_tile_word(row, cc * 4)]) = val;
-  }
-  __syncthreads();
-  const int lane = t & 63, g = lane & 7;
-  const int p = 8 * (t >> 6) + (lane >> 3);
-  uint32_t d[16];
-  us2 m = {0, 0};
+  };
+  // A workgroup takes blocks blockIdx.x, blockIdx.x + gridDim.x, ...; the
+  // next block's loads fly while this block is reduced and stored.
+  int64_t blk = blockIdx.x;
+  if (blk < nblocks) load_block(blk);
+  for (; blk < nblocks; blk += gridDim.x) {
+    const int64_t rb = blk / ncb;
+    const int64_t c0 = (blk % ncb) * 64;
+    const int64_t r0 = rb * 128;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    d[i] = tile[cols_tile_word(16 * g + i, p)];
-    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[i] & 0x7FFF7FFFu));
-  }
-  const uint32_t mm = row8_max_pk_u16(__builtin_bit_cast(uint32_t, m));
-  uint4 outs[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t tt = h ? (mm >> 16) : (mm & 0xFFFFu);
-    const float s = tile_scale(tt);
-    float y[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = h ? bf16_hi(d[i]) : bf16_lo(d[i]);
-    uint4 out;
-    if (tt < kBf16InfAbs) {
-      const float r = 1.0f / s;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = div_by_scale(y[i], s, r);
-      out.x = pack4_sat(y[0], y[1], y[2], y[3]);
-      out.y = pack4_sat(y[4], y[5], y[6], y[7]);
-      out.z = pack4_sat(y[8], y[9], y[10], y[11]);
-      out.w = pack4_sat(y[12], y[13], y[14], y[15]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = y[i] / s;
-      out.x = pack4_sat_nan(y[0], y[1], y[2], y[3]);
-      out.y = pack4_sat_nan(y[4], y[5], y[6], y[7]);
-      out.z = pack4_sat_nan(y[8], y[9], y[10], y[11]);
-      out.w = pack4_sat_nan(y[12], y[13], y[14], y[15]);
+    for (int i = 0; i < 4; ++i) {
+      const int ci = t + 256 * i;
+      const int row = ci >> 3, cc = ci & 7;
+      *reinterpret_cast<uint4*>(&tile[cols_tile_word(row, cc * 4)]) = vals[i];
     }
-    outs[h] = out;
-    const int64_t col = c0 + 2 * p + h;
-    if (col < cols) {
-      if constexpr (!kTiled) *reinterpret_cast<uint4*>(q + transposed_code_offset<false>(col, rb, g, ldq, nbr)) = out;
-      if (g == 0) {
-        scales[rb * ld_s + col] = s;
-        if (amax_out) amax_out[rb * ld_s + col] = amax_value(tt);
+    if (blk + gridDim.x < nblocks) load_block(blk + gridDim.x);
+    __syncthreads();
+    const int lane = t & 63, g = lane & 7;
+    const int p = 8 * (t >> 6) + (lane >> 3);
+    uint32_t d[16];
+    us2 m = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      d[i] = tile[cols_tile_word(16 * g + i, p)];
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, d[i] & 0x7FFF7FFFu));
+    }
+    const uint32_t mm = row8_max_pk_u16(__builtin_bit_cast(uint32_t, m));
+    uint4 outs[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t tt = h ? (mm >> 16) : (mm & 0xFFFFu);
+      const float s = tile_scale(tt);
+      float y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = h ? bf16_hi(d[i]) : bf16_lo(d[i]);
+      uint4 out;
+      if (tt < kBf16InfAbs) {
+        const float r = 1.0f / s;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = div_by_scale(y[i], s, r);
+        out.x = pack4_sat(y[0], y[1], y[2], y[3]);
+        out.y = pack4_sat(y[4], y[5], y[6], y[7]);
+        out.z = pack4_sat(y[8], y[9], y[10], y[11]);
+        out.w = pack4_sat(y[12], y[13], y[14], y[15]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = y[i] / s;
+        out.x = pack4_sat_nan(y[0], y[1], y[2], y[3]);
+        out.y = pack4_sat_nan(y[4], y[5], y[6], y[7]);
+        out.z = pack4_sat_nan(y[8], y[9], y[10], y[11]);
+        out.w = pack4_sat_nan(y[12], y[13], y[14], y[15]);
+      }
+      outs[h] = out;
+      const int64_t col = c0 + 2 * p + h;
+      if (col < cols) {
+        if constexpr (!kTiled) *reinterpret_cast<uint4*>(q + transposed_code_offset<false>(col, rb, g, ldq, nbr)) = out;
+        if (g == 0) {
+          scales[rb * ld_s + col] = s;
+          if (amax_out) amax_out[rb * ld_s + col] = amax_value(tt);
+        }
       }
     }
+    // tiled output: cols % 128 == 0, so both columns exist
+    if constexpr (kTiled) store_pair_tiled<false>(q, outs[0], outs[1], c0 + 2 * p, rb, g, nbr);
+    __syncthreads();   // the next block overwrites the tile
   }
-  // tiled output: cols % 128 == 0, so both columns exist
-  if constexpr (kTiled) store_pair_tiled<false>(q, outs[0], outs[1], c0 + 2 * p, rb, g, nbr);
 }
 
 // ---------------------------------------------------------------------------
@@ -545,12 +563,13 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int6
   const int64_t ncb = (cols + 63) / 64;
   const int64_t nblocks = (rows / 128) * ncb;
   const int64_t nbr = rows / 128;
+  const int64_t grid = (nblocks + 1) / 2;      // two blocks per workgroup
   if (tiled)
-    hipLaunchKernelGGL(quant_cols_kernel<true>, dim3((unsigned)nblocks), dim3(256), 0, stream,
-                       x, cols, ldx, ncb, nbr, q, ldq, scales, ld_s, amax_out);
+    hipLaunchKernelGGL(quant_cols_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       x, cols, ldx, ncb, nbr, nblocks, q, ldq, scales, ld_s, amax_out);
   else
-    hipLaunchKernelGGL(quant_cols_kernel<false>, dim3((unsigned)nblocks), dim3(256), 0, stream,
-                       x, cols, ldx, ncb, nbr, q, ldq, scales, ld_s, amax_out);
+    hipLaunchKernelGGL(quant_cols_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       x, cols, ldx, ncb, nbr, nblocks, q, ldq, scales, ld_s, amax_out);
   return hipGetLastError();
 }
 

@@ -86,6 +86,7 @@ class Timer:
         self.pending = []
         self.acc = {}
         self.count = {}
+        self.samples = {}
 
     def region(self, name, fn):
         ev0 = self.torch.cuda.Event(enable_timing=True)
@@ -99,17 +100,25 @@ class Timer:
     def collect(self):
         self.torch.cuda.synchronize()
         for name, a, b in self.pending:
-            self.acc[name] = self.acc.get(name, 0.0) + a.elapsed_time(b)
+            t = a.elapsed_time(b)
+            self.acc[name] = self.acc.get(name, 0.0) + t
+            self.samples.setdefault(name, []).append(t)
             self.count[name] = self.count.get(name, 0) + 1
         self.pending.clear()
 
     def mean_ms(self, name):
         return self.acc[name] / self.count[name]
 
+    def spread_ms(self, name):
+        """(median, p10, p90) of the region over the timed steps."""
+        v = np.sort(np.asarray(self.samples[name]))
+        return float(np.median(v)), float(np.quantile(v, 0.1)), float(np.quantile(v, 0.9))
+
     def reset(self):
         self.pending.clear()
         self.acc.clear()
         self.count.clear()
+        self.samples.clear()
 
 
 def traffic_from_profiles(record, kernel_src):
@@ -145,9 +154,46 @@ def cpu_baseline(x_bits, w_bits, sample_rows):
     dt = time.perf_counter() - t0
     flop = 2.0 * sample_rows * Ns * K
     cores = len(os.sched_getaffinity(0))
+    # the quantizer oracle alone on one core (numpy runs it single-threaded)
+    qrows = min(1024, sample_rows)
+    t1 = time.perf_counter()
+    quant.quant_rows(xb[:qrows])
+    dq = time.perf_counter() - t1
+    qbytes = qrows * K * (3 + 4 / 128)
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = ""
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {}).get("name", "")
+    except Exception:
+        pass
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"1x128 quant of {sample_rows}x{K} X rows + float64 block GEMM against "
-                      f"{Ns}x{K} pre-quantized W ({flop:.3e} FLOP, {dt:.1f} s)"}
+                      f"{Ns}x{K} pre-quantized W ({flop:.3e} FLOP, {dt:.1f} s)",
+            "quantizer_oracle_GB/s_1core": qbytes / dq / 1e9,
+            "quantizer_sample": f"{qrows}x{K} rows, {dq:.2f} s",
+            "cpu_model": cpu_model, "blas": blas}
+
+
+def device_info():
+    """Engine clock and power cap as rocm-smi reports them (read-only; empty if
+    the tool is missing or slow)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--showmaxpower", "--json"],
+                             capture_output=True, text=True, timeout=20).stdout
+        card = next(iter(json.loads(out).values()))
+        keep = {k: v for k, v in card.items() if "sclk" in k.lower() or "power" in k.lower()}
+        return keep
+    except Exception:
+        return {}
 
 
 def main():
@@ -346,7 +392,9 @@ def main():
                          "TFLOP/s_incl_quant": value, "TFLOP/s_gemm": F3 / tg / 1e9,
                          "quant_GB/s": 4096 * 7168 * (3 + 4 / 128) / tq / 1e6,
                          "weights": "operand-tiled codes",
-                         "ms_gemm_rowmajor_weights": trm, "TFLOP/s_gemm_rowmajor_weights": F3 / trm / 1e9}
+                         "ms_gemm_rowmajor_weights": trm, "TFLOP/s_gemm_rowmajor_weights": F3 / trm / 1e9,
+                         "ms_gemm_median_p10_p90": tm.spread_ms("fprop.gemm"),
+                         "ms_quant_plus_gemm_median_p10_p90": tm.spread_ms("fprop")}
         # the kernel's mean launch duration over the timed steps (HIP events
         # around each launch on its stream); the back-to-back batch after the
         # steps runs under sustained power and is reported beside it
@@ -443,7 +491,8 @@ def main():
         "dtype": "fp8e4m3 (fp32 accumulate)",
         "data": "synthetic",
         "config": {"workload": "fprop: 1x128 quant of X 4096x7168 + block-scaled FP8 GEMM "
-                               "Y=X W^T 4096x18432x7168, BF16 out (W pre-quantized 128x128)",
+                               "Y=X W^T 4096x18432x7168, BF16 out (W pre-quantized 128x128, "
+                               "operand-tiled codes)",
                    "M": 4096, "N": 18432, "K": 7168},
         "roofline": roofline,
         "roofline_quantizer": ({"bound": "hbm", "achieved": QB / batch["quantizer"] / 1e6, "peak": PEAK_HBM_GBPS,
@@ -456,6 +505,7 @@ def main():
                                 "kernel": "quant_rows_kernel<online> 8192x7168"}
                                if "quantizer" in rows else None),
         "cpu_baseline": cpu,
+        "device": device_info(),
         "rows": rows,
     }
     print(json.dumps(out), flush=True)

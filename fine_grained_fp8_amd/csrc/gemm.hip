@@ -39,6 +39,8 @@
 //    the way into the MFMA operand registers.
 //  * Workgroup ids are remapped so each XCD (ids congruent mod 8) walks a
 //    contiguous, M-grouped run of tiles and its private L2 sees the reuse.
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -182,6 +184,13 @@ template <int vm>
 __device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(vm >= 0 && vm < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14));
+}
+
+// the same with no wait on the LDS / scalar-memory counter
+template <int vm>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(vm >= 0 && vm < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14));
 }
 
 template <int kLayout, bool kOutF32, bool kGrouped>
@@ -557,81 +566,93 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     for (int j = 0; j < DNJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   v8i w0[DNI], w1[DNI], w2[DNI], w3[DNI];
 
-  // ---- one K block: token tile in stage st, weights in wc; block kb+3
-  // streams into stage sf (read in step kb-1) and registers wf ----
-  // Issue order: the token tile and scales of block kb+2 (DMA), then the
-  // weights of block kb+3, in every step.  At the start of step kb the ops
-  // issued after block kb's DMA are block kb+1's weights and all of step
-  // kb-1, so vmcnt(kDOpsPerBlock + kDWOps) marks block kb's tile and weights
-  // landed.  (The compiler does not count the LDS-DMA instructions in its own
-  // waits for the weight registers; with this order its stricter waits only
-  // cover data that is needed by then anyway.)
-  auto step = [&](int kb, const uint8_t* st, v8i (&wc)[DNI], uint8_t* sd, v8i (&wf)[DNI]) {
-    wait_vm_lgkm0<kDOpsPerBlock + kDWOps>();
-    __builtin_amdgcn_sched_barrier(0);
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    const bool live = kb < KB;
+  // ---- one K block per step: token tile in stage st, weights in wc ----
+  // Issue order of the global loads: the token tile and scales of block kb+2
+  // (DMA, rows 0-2), then the weights of block kb+3 (rows 3-6), in every
+  // step.  After row kMid the wave waits for block kb+1 (its DMA was issued
+  // in step kb-1 and only block kb+2's weights and this step's first
+  // 2 (kMid + 1) loads came after it), passes the workgroup barrier, and
+  // reads block kb+1's scales and first two token-side operand rows while
+  // rows kMid+1.. of block kb still run on the matrix unit, so the next step
+  // starts with its operands in registers.  The partial sums of a block's
+  // last row are folded in the next step's first row.  Stage safety with four
+  // stages: the DMA of step kb writes the stage of block kb-2, whose last
+  // reads (step kb-2) every wave finished before the barrier of step kb-1.
+  // (The compiler does not count the LDS-DMA instructions in its own waits
+  // for the weight registers; with this order its stricter waits only cover
+  // data that is needed by then anyway.)
+  constexpr int kMid = 5;
+  v8i bxa, bxb;                     // block kb+1: token-side operand rows 0, 1
+  float tn[DNJ];                    // block kb+1: token-side scales
+  float wn = 1.f;                   // block kb+1: weight-side block scale
+  v4f Pl[DNI];                      // last row of partial sums of block kb-1
+  float cl = 0.f;                   // and its scale
+#pragma unroll
+  for (int i = 0; i < DNI; ++i) Pl[i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto prefetch = [&](const uint8_t* stn) {
+    const float* sxl = reinterpret_cast<const float*>(stn + kDScaleOff);
+    const float* swl = reinterpret_cast<const float*>(stn + kDWScaleOff);
+    if constexpr (kBlockW) wn = swl[wave * 64];
+#pragma unroll
+    for (int j = 0; j < DNJ; ++j) tn[j] = sxl[j * 16 + lrow];
+    bxa = pair(stn + x_lo, stn + x_hi);
+    bxb = pair(stn + x_lo + 2048, stn + x_hi + 2048);
+  };
+
+  auto step = [&](auto pad_tag, int kb, const uint8_t* st, v8i (&wc)[DNI], const uint8_t* stn,
+                  uint8_t* sd, v8i (&wf)[DNI]) {
+    constexpr bool kPad = decltype(pad_tag)::value;   // the round may hold padding steps
+    const bool live = !kPad || kb < KB;
     const int kb_d = kb + 2 < KB ? kb + 2 : KB - 1;   // token tile streamed this step
     const int kb_w = kb + 3 < KB ? kb + 3 : KB - 1;   // weights streamed this step
 
-    const float* sxl = reinterpret_cast<const float*>(st + kDScaleOff);
-    const float* swl = reinterpret_cast<const float*>(st + kDWScaleOff);
-    float wsc = 1.f;
-    if constexpr (kBlockW) wsc = swl[wave * 64];
-    // scales first: their LDS reads complete ahead of the operand reads, so
-    // the waits for them do not wait for the operands
     float c[DNJ];
 #pragma unroll
     for (int j = 0; j < DNJ; ++j) {
-      const float t = sxl[j * 16 + lrow];
-      c[j] = live ? (kLayout == kWgrad ? t : t * wsc) : 0.f;
+      const float t = kBlockW ? tn[j] * wn : tn[j];
+      c[j] = live ? t : 0.f;
     }
     float4 rs[DNI];
     if constexpr (kLayout == kWgrad) {
+      const float* swl = reinterpret_cast<const float*>(st + kDWScaleOff);
 #pragma unroll
       for (int i = 0; i < DNI; ++i)
         rs[i] = *reinterpret_cast<const float4*>(swl + wave * 64 + i * 16 + lgrp * 4);
     }
-    __asm__ volatile("" ::: "memory");
-    // token-side operands two rows ahead of their MFMAs: a burst of all 16
-    // reads would fill the LDS queue and stall the wave at issue
-    v8i bx[DNJ];
-    bx[0] = pair(st + x_lo, st + x_hi);
-    bx[1] = pair(st + x_lo + 2048, st + x_hi + 2048);
-
-    auto fold = [&](int j, int i, const v4f& P) {
+    auto fold = [&](v4f& a, const v4f& P, float cj, int i) {
       if constexpr (kLayout == kWgrad) {
-        acc[i][j][0] = __builtin_fmaf(P[0] * rs[i].x, c[j], acc[i][j][0]);
-        acc[i][j][1] = __builtin_fmaf(P[1] * rs[i].y, c[j], acc[i][j][1]);
-        acc[i][j][2] = __builtin_fmaf(P[2] * rs[i].z, c[j], acc[i][j][2]);
-        acc[i][j][3] = __builtin_fmaf(P[3] * rs[i].w, c[j], acc[i][j][3]);
+        a[0] = __builtin_fmaf(P[0] * rs[i].x, cj, a[0]);
+        a[1] = __builtin_fmaf(P[1] * rs[i].y, cj, a[1]);
+        a[2] = __builtin_fmaf(P[2] * rs[i].z, cj, a[2]);
+        a[3] = __builtin_fmaf(P[3] * rs[i].w, cj, a[3]);
       } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(P[v], c[j], acc[i][j][v]);
+        for (int v = 0; v < 4; ++v) a[v] = __builtin_fmaf(P[v], cj, a[v]);
       }
     };
+
+    v8i bx[DNJ];
+    bx[0] = bxa;
+    bx[1] = bxb;
     // rows j of 4 MFMAs (the wave's 4 weight subtiles against token subtile
     // j), each MFMA followed by the fold of the same subtile's partial from
-    // row j-1 (issued four MFMAs earlier); two of block kb+3's loads per row
+    // row j-1 (row 0: the previous block's last row); two loads per row
     v4f P0[DNI], P1[DNI];
-    // operands in AGPRs (the MFMA reads them there), leaving the VGPRs to the
-    // accumulators, the partial sums and the scales
-#pragma unroll
-    for (int i = 0; i < DNI; ++i) __asm__ volatile("" : "+a"(wc[i]));
+    // the operands stay in whichever register file the allocator gave them
+    // (the MFMA reads both); pinning them to AGPRs costs a copy per register
+    // of every weight buffer that crosses the loop's back edge
 #pragma unroll
     for (int j = 0; j < DNJ; ++j) {
       v4f (&Pc)[DNI] = (j & 1) ? P1 : P0;
       v4f (&Pp)[DNI] = (j & 1) ? P0 : P1;
       if (j + 2 < DNJ) bx[j + 2] = pair(st + x_lo + (j + 2) * 2048, st + x_hi + (j + 2) * 2048);
-      __asm__ volatile("" : "+a"(bx[j]));
 #pragma unroll
       for (int i = 0; i < DNI; ++i) {
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
         Pc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wc[i], bx[j], zero, 0, 0, 0, 127, 0, 127);
-        if (j > 0) fold(j - 1, i, Pp[i]);
+        if (j > 0) fold(acc[i][j - 1], Pp[i], c[j - 1], i);
+        else if constexpr (kBlockW) fold(acc[i][DNJ - 1], Pl[i], cl, i);
         // instruction order = source order: one MFMA, then the fold of the
         // partial it produced four MFMAs (20 instructions) earlier
         __builtin_amdgcn_sched_barrier(0);
@@ -640,15 +661,30 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
         issue_load(2 * j < kDDmaOps ? kb_d : kb_w, 2 * j, sd, wf);
         issue_load(2 * j + 1 < kDDmaOps ? kb_d : kb_w, 2 * j + 1, sd, wf);
       }
+      if (j == kMid) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<kDWOps + 2 * (kMid + 1)>();
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        prefetch(stn);
+      }
     }
+    if constexpr (kBlockW) {
 #pragma unroll
-    for (int i = 0; i < DNI; ++i) fold(DNJ - 1, i, ((DNJ - 1) & 1) ? P1[i] : P0[i]);
+      for (int i = 0; i < DNI; ++i) Pl[i] = ((DNJ - 1) & 1) ? P1[i] : P0[i];
+      cl = c[DNJ - 1];
+    } else {
+#pragma unroll
+      for (int i = 0; i < DNI; ++i) fold(acc[i][DNJ - 1], ((DNJ - 1) & 1) ? P1[i] : P0[i], c[DNJ - 1], i);
+    }
 #pragma unroll
     for (int j = 0; j < DNJ; ++j) {
 #pragma unroll
       for (int i = 0; i < DNI; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (j > 0) __builtin_amdgcn_sched_group_barrier(0x002, kLayout == kWgrad ? 8 : 4, 0);
+        if (j > 0 || kBlockW) __builtin_amdgcn_sched_group_barrier(0x002, kLayout == kWgrad ? 8 : 4, 0);
         if (i == 0 && j + 2 < DNJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         if ((i & 1) && j < kDOpsPerBlock / 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
@@ -657,9 +693,10 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
 
   // Prologue, in the steady-state order (weights of block 0; tile of block 0
   // and weights of block 1; tile of block 1 and weights of block 2), blocks
-  // past K repeating the last block.  Then whole rounds of four steps with no
-  // conditions inside: K is padded to a multiple of four blocks and a padding
-  // step folds with scale 0.
+  // past K repeating the last block; then block 0's first operands.  Whole
+  // rounds of four steps follow with no conditions inside; when K is not a
+  // multiple of four blocks the last round pads with steps that fold with
+  // scale 0.
   {
     auto clamp = [&](int b) { return b < KB ? b : KB - 1; };
 #pragma unroll
@@ -672,16 +709,36 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     for (int op = 0; op < kDDmaOps; ++op) issue_load(clamp(1), op, lds_s1, w1);
 #pragma unroll
     for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(2), op, lds_s2, w2);
+    wait_vm<kDDmaOps + 2 * kDWOps>();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    prefetch(lds_s0);
   }
-  for (int kb = 0; kb < KB; kb += 4) {
-    step(kb, lds_s0, w0, lds_s2, w3);
-    step(kb + 1, lds_s1, w1, lds_s3, w0);
-    step(kb + 2, lds_s2, w2, lds_s0, w1);
-    step(kb + 3, lds_s3, w3, lds_s1, w2);
+  using no_pad = std::integral_constant<bool, false>;
+  using pad = std::integral_constant<bool, true>;
+  const int KB4 = KB & ~3;
+  int kb = 0;
+  for (; kb < KB4; kb += 4) {
+    step(no_pad{}, kb, lds_s0, w0, lds_s1, lds_s2, w3);
+    step(no_pad{}, kb + 1, lds_s1, w1, lds_s2, lds_s3, w0);
+    step(no_pad{}, kb + 2, lds_s2, w2, lds_s3, lds_s0, w1);
+    step(no_pad{}, kb + 3, lds_s3, w3, lds_s0, lds_s1, w2);
+  }
+  if (kb < KB) {
+    step(pad{}, kb, lds_s0, w0, lds_s1, lds_s2, w3);
+    step(pad{}, kb + 1, lds_s1, w1, lds_s2, lds_s3, w0);
+    step(pad{}, kb + 2, lds_s2, w2, lds_s3, lds_s0, w1);
+    step(pad{}, kb + 3, lds_s3, w3, lds_s0, lds_s1, w2);
+  }
+  if constexpr (kBlockW) {
+#pragma unroll
+    for (int i = 0; i < DNI; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][DNJ - 1][v] = __builtin_fmaf(Pl[i][v], cl, acc[i][DNJ - 1][v]);
   }
   // the last steps' reload DMA must land before the workgroup's LDS is released
   wait_vm_lgkm0<0>();
-
   // ---- epilogue: lane holds 4 consecutive n of row m for every (i, j) ----
 #pragma unroll
   for (int j = 0; j < DNJ; ++j) {

@@ -183,17 +183,24 @@ def cpu_baseline(x_bits, w_bits, sample_rows):
 
 
 def device_info():
-    """Engine clock and power cap as rocm-smi reports them (read-only; empty if
-    the tool is missing or slow)."""
-    import subprocess
+    """Engine-clock levels and power cap of the first GPU, read from sysfs
+    (no helper process is started; empty where the files are missing)."""
+    import glob
+    info = {}
     try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--showmaxpower", "--json"],
-                             capture_output=True, text=True, timeout=20).stdout
-        card = next(iter(json.loads(out).values()))
-        keep = {k: v for k, v in card.items() if "sclk" in k.lower() or "power" in k.lower()}
-        return keep
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            sclk = os.path.join(dev, "pp_dpm_sclk")
+            if not os.path.exists(sclk):
+                continue
+            with open(sclk) as f:
+                info["sclk_levels"] = [l.strip() for l in f if l.strip()]
+            for cap in glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_cap")):
+                with open(cap) as f:
+                    info["power_cap_W"] = int(f.read().strip()) / 1e6
+            break
     except Exception:
-        return {}
+        pass
+    return info
 
 
 def main():

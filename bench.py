@@ -35,7 +35,7 @@ seeded synthetic inputs already resident in HBM:
 quantization (2*M*N*K / (t_quant + t_gemm)), from HIP events on the launch
 stream averaged over the timed steps.  Other rows are reported under "rows".
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K (50)] [--warmup W (10)] [--gpus 1] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -63,8 +63,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=2048)
     ap.add_argument("--only", default="", help="comma list of rows to run (default all)")
@@ -182,6 +182,38 @@ def cpu_baseline(x_bits, w_bits, sample_rows):
             "cpu_model": cpu_model, "blas": blas}
 
 
+_X_SHARED = None   # the rows the pool workers quantize (inherited through fork)
+
+
+def _quant_rows_chunk(bounds):
+    from oracle import quant
+    lo, hi = bounds
+    t = time.perf_counter()
+    quant.quant_rows(_X_SHARED[lo:hi])
+    return time.perf_counter() - t
+
+
+def quant_oracle_all_cores(x_bits):
+    """The quantizer oracle over `x_bits` split into row chunks on a fork-based
+    process pool, one process per core (at most 16); run before anything
+    touches the GPU, so the forked workers inherit no device state."""
+    import multiprocessing as mp
+    global _X_SHARED
+    _X_SHARED = x_bits
+    procs = max(1, min(16, len(os.sched_getaffinity(0))))
+    edges = np.linspace(0, x_bits.shape[0], 4 * procs + 1).astype(int)
+    chunks = [(int(a), int(b)) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+    with mp.get_context("fork").Pool(procs) as pool:
+        pool.map(_quant_rows_chunk, [(0, 8)] * procs)   # workers import the oracle
+        t0 = time.perf_counter()
+        pool.map(_quant_rows_chunk, chunks)
+        dt = time.perf_counter() - t0
+    _X_SHARED = None
+    nbytes = x_bits.size * (3 + 4 / 128)
+    return {"quantizer_oracle_GB/s_all_cores": nbytes / dt / 1e9, "quantizer_all_cores_procs": procs,
+            "quantizer_all_cores_sample": f"{x_bits.shape[0]}x{x_bits.shape[1]} rows, {dt:.2f} s"}
+
+
 def device_info():
     """Engine-clock levels and power cap of the first GPU, read from sysfs
     (no helper process is started; empty where the files are missing)."""
@@ -210,17 +242,22 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    import synthetic as syn
+    only = set(s for s in args.only.split(",") if s)
+    want = (lambda r: not only or r in only)
+    cpu_pool = None
+    if not args.no_cpu_baseline and want("fprop"):
+        # before the GPU is touched: the forked pool workers must not inherit it
+        log("timing the quantizer oracle on all host cores ...")
+        cpu_pool = quant_oracle_all_cores(syn.activation_with_outliers(4096, 7168, seed=0))
+
     import torch
     import fine_grained_fp8_amd as fp8
-    import synthetic as syn
 
     fp8.load_library()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    only = set(s for s in args.only.split(",") if s)
-    want = (lambda r: not only or r in only)
-
     # ---------------- inputs (seeded, synthetic, resident in HBM) ----------------
     t0 = time.time()
     d = {}
@@ -480,6 +517,8 @@ def main():
     if not args.no_cpu_baseline and want("fprop"):
         log("timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(host["x3"], host["w3"], args.cpu_sample_rows)
+        if cpu_pool:
+            cpu.update(cpu_pool)
 
     if value is None and "quantizer" in rows:
         value = rows["quantizer"]["GB/s"]

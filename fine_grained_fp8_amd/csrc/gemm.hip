@@ -740,6 +740,62 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   // the last steps' reload DMA must land before the workgroup's LDS is released
   wait_vm_lgkm0<0>();
   // ---- epilogue: lane holds 4 consecutive n of row m for every (i, j) ----
+  if (rows_m == BM && rows_n == BN) {
+    // Full tile: the wave's 64 (n) x 128 (m) block goes through its own stage
+    // array (free once every wave has passed this barrier) so that every
+    // store instruction writes whole row segments of the output: 8 rows x
+    // 128 B (BF16) or 4 rows x 256 B (FP32, in two halves of 64 rows).  Lane
+    // stores of 4 values per row took ~2.5x as long, all workgroups of a round
+    // storing at once.  16-byte chunks are XOR-swizzled by row.
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    uint8_t* ob = wave == 0 ? lds_s0 : (wave == 1 ? lds_s1 : (wave == 2 ? lds_s2 : lds_s3));
+    if constexpr (!kOutF32) {
+#pragma unroll
+      for (int j = 0; j < DNJ; ++j) {
+#pragma unroll
+        for (int i = 0; i < DNI; ++i) {
+          const int m = j * 16 + lrow, nl = i * 16 + lgrp * 4;
+          const v4f& r = acc[i][j];
+          const __bf16 h0 = (__bf16)r[0], h1 = (__bf16)r[1], h2 = (__bf16)r[2], h3 = (__bf16)r[3];
+          const uint32_t u0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          const uint32_t u1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+          *reinterpret_cast<uint2*>(ob + m * 128 + (((nl >> 3) ^ (m & 7)) << 4) + (nl & 7) * 2) =
+              make_uint2(u0, u1);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < BM / 8; ++t) {
+        const int row = t * 8 + (lane >> 3), ch = lane & 7;
+        const uint4 v = *reinterpret_cast<const uint4*>(ob + row * 128 + ((ch ^ (row & 7)) << 4));
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.C) + (m0 + row) * p.ldc + n0 + wave * 64 + ch * 8;
+        *reinterpret_cast<uint4*>(dst) = v;
+      }
+    } else {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int j = 0; j < DNJ / 2; ++j) {
+#pragma unroll
+          for (int i = 0; i < DNI; ++i) {
+            const int m = j * 16 + lrow, ch = i * 4 + lgrp;
+            const v4f& r = acc[i][half * (DNJ / 2) + j];
+            *reinterpret_cast<float4*>(ob + m * 256 + ((ch ^ (m & 15)) << 4)) = make_float4(r[0], r[1], r[2], r[3]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < BM / 8; ++t) {
+          const int row = t * 4 + (lane >> 4), ch = lane & 15;
+          const float4 v = *reinterpret_cast<const float4*>(ob + row * 256 + ((ch ^ (row & 15)) << 4));
+          float* dst = reinterpret_cast<float*>(p.C) + (m0 + half * (BM / 2) + row) * p.ldc + n0 + wave * 64 + ch * 4;
+          *reinterpret_cast<float4*>(dst) = v;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < DNJ; ++j) {
     const int64_t m = m0 + j * 16 + lrow;

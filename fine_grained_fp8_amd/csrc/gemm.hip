@@ -39,6 +39,7 @@
 //    the way into the MFMA operand registers.
 //  * Workgroup ids are remapped so each XCD (ids congruent mod 8) walks a
 //    contiguous, M-grouped run of tiles and its private L2 sees the reuse.
+#include <atomic>
 #include <type_traits>
 
 #include "device.hpp"
@@ -111,14 +112,16 @@ __device__ __forceinline__ v8i read_operand_t(const uint8_t* tile, int n_sub, in
   return out;
 }
 
-// Tile of workgroup `blockIdx.x`: token rows [m0, min(m0 + BM, m_end)) and
-// output columns [n0, n0 + BN); Bp / sBp point at the tile's group in the
-// grouped case.  Returns false for the padding workgroups of a grouped launch.
+// Tile `id` of a launch of `ids` tile ids: token rows [m0, min(m0 + BM,
+// m_end)) and output columns [n0, n0 + BN); Bp / sBp point at the tile's
+// group in the grouped case.  Returns false for the padding ids of a grouped
+// launch.
 __device__ __forceinline__ bool decode_tile(const GemmProblem& p, int64_t total_tiles, bool grouped,
+                                            int64_t id, int64_t ids,
                                             int64_t& m0, int64_t& m_end, int64_t& n0,
                                             const uint8_t*& Bp, const float*& sBp) {
   const int64_t tiles_n = (p.N + BN - 1) / BN;
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t b = xcd_remap(id, ids);
   Bp = p.B;
   sBp = p.sB;
   if (grouped) {
@@ -152,6 +155,18 @@ __device__ __forceinline__ bool decode_tile(const GemmProblem& p, int64_t total_
 
 // Round and store 4 consecutive outputs (n..n+3) of row m; columns past N
 // are dropped.
+// Values every lane holds alike, pinned to scalar registers (the tile
+// decode runs 64-bit divisions on the vector unit).
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* v) {
+  return reinterpret_cast<T*>(uniform_i64(reinterpret_cast<int64_t>(v)));
+}
+
 template <bool kOutF32>
 __device__ __forceinline__ void store4(const GemmProblem& p, int64_t m, int64_t n, const v4f& r) {
   if constexpr (kOutF32) {
@@ -213,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
   int64_t m0, m_end, n0;
   const uint8_t* Bp;
   const float* sBp;
-  if (!decode_tile(p, total_tiles, kGrouped, m0, m_end, n0, Bp, sBp)) return;
+  if (!decode_tile(p, total_tiles, kGrouped, blockIdx.x, gridDim.x, m0, m_end, n0, Bp, sBp)) return;
   const int KB = (int)(p.K / BK);
   const int rows_m = (int)(m_end - m0 < BM ? m_end - m0 : BM);   // valid token rows in the tile
   const int rows_n = (int)(p.N - n0 < BN ? p.N - n0 : BN);       // valid output columns
@@ -471,42 +486,46 @@ constexpr int DNI = 4, DNJ = 8;                // wave tile: 64 (n) x 128 (m)
 constexpr int kDScaleOff = BM * BK;            // token-side scales (1 KB DMA footprint)
 constexpr int kDWScaleOff = kDScaleOff + 1024; // weight-side scales (1 KB)
 constexpr int kDStage = kDWScaleOff + 1024;    // 18 KB per stage
+constexpr int kDOutStage = 16384;              // epilogue staging per wave: 128 x 64 BF16 or 64 x 64 FP32
 constexpr int kDDmaOps = 4 + 1 + 1;            // DMA per block: 4 token-row, 2 scale instructions
 constexpr int kDWOps = 8;                      // weight loads per block
 constexpr int kDOpsPerBlock = kDDmaOps + kDWOps;
 
 template <int kLayout, bool kOutF32, bool kGrouped, bool kTiledB>
-__global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProblem p, int64_t total_tiles) {
+__global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProblem p, int64_t total_tiles,
+                                                                        int64_t tile_ids) {
   static_assert(kLayout != kDgrad, "Dgrad reads the weights transposed through LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s0[kDStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s1[kDStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s2[kDStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_s3[kDStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_out[4][kDOutStage];   // per-wave epilogue staging
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15, lgrp = lane >> 4;
 
-  int64_t m0, m_end, n0;
-  const uint8_t* Bp;
-  const float* sBp;
-  if (!decode_tile(p, total_tiles, kGrouped, m0, m_end, n0, Bp, sBp)) return;
+  // Persistent: the workgroup takes tile ids blockIdx.x, + gridDim.x, ... of
+  // the launch's `tile_ids` (gridDim.x is a multiple of 8, so all ids of a
+  // workgroup map to the same XCD's run of tiles), and starts the loads of its
+  // next tile before it stores the current one.
   const int KB = (int)(p.K / BK);
-  const int rows_m = (int)(m_end - m0 < BM ? m_end - m0 : BM);
-  const int rows_n = (int)(p.N - n0 < BN ? p.N - n0 : BN);
-
+  constexpr bool kBlockW = kLayout == kFprop || kLayout == kDgradT;
+  int64_t m0 = 0, m_end = 0, n0 = 0;
+  const uint8_t* Bp = p.B;
+  const float* sBp = p.sB;
+  int rows_m = 0, rows_n = 0;
+  __amdgpu_buffer_rsrc_t rsrc_x, rsrc_w, rsrc_sw;
+  uint32_t sw_off = 0;
   // token-side tile: rows m0.., DMA'd 8 rows x 128 B per instruction, 16-byte
   // chunks XOR-swizzled by row & 7 (row & 7 == (lane >> 3) & 7 here)
-  const __amdgpu_buffer_rsrc_t rsrc_x = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.A + m0 * p.lda), (short)0, rows_m * (int)p.lda, (int)kRsrcWord3);
   const int xrow = wave * 32 + (lane >> 3);
   const uint32_t off_x = (uint32_t)(xrow * (int)p.lda + (((lane & 7) ^ (lane >> 3)) << 4));
-  // weight-side rows n0 + 64 wave + 16 i + lrow, loaded straight into registers
-  const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(Bp + n0 * p.ldb), (short)0, rows_n * (int)p.ldb, (int)kRsrcWord3);
-  // row-major: lane reads 16 B of its row; operand-tiled (ldb == K): the
-  // wave's 16-row groups are 2 KB tiles per K block, each half one 1 KB run
+  // weight-side rows n0 + 64 wave + 16 i + lrow, loaded straight into
+  // registers; row-major: lane reads 16 B of its row; operand-tiled (ldb ==
+  // K): the wave's 16-row groups are 2 KB tiles per K block, each half one
+  // 1 KB run
   const uint32_t off_w = kTiledB ? (uint32_t)(wave * 4 * KB * 2048 + lane * 16)
                                  : (uint32_t)((wave * 64 + lrow) * (int)p.ldb + lgrp * 16);
   const uint32_t w_istride = kTiledB ? (uint32_t)(KB * 2048) : (uint32_t)(16 * p.ldb);
@@ -516,14 +535,31 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   // (every lane fetches the same float; Fprop's table is [N/128][K/128],
   // Dgrad_T reads the forward table [K/128][N/128]); Wgrad - the workgroup's
   // 256 per-column scales
-  constexpr bool kBlockW = kLayout == kFprop || kLayout == kDgradT;
   const int64_t sw_elems = kLayout == kFprop ? (p.N / 128) * p.ld_sb
                                              : (kLayout == kDgradT ? (p.K / BK) * p.ld_sb : 0);
-  const __amdgpu_buffer_rsrc_t rsrc_sw = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)sBp, (short)0, (int)(sw_elems * 4), (int)kRsrcWord3);
-  const int64_t nbw = (n0 + 64 * wave) / 128;
-  const uint32_t sw_off = kLayout == kFprop ? (uint32_t)(nbw * p.ld_sb) * 4u : (uint32_t)nbw * 4u;
   const uint32_t sw_kstride = kLayout == kFprop ? 4u : (uint32_t)p.ld_sb * 4u;
+  // decode tile id `id` and set up its buffer resources; false for padding ids
+  auto setup_tile = [&](int64_t id) -> bool {
+    if (!decode_tile(p, total_tiles, kGrouped, id, tile_ids, m0, m_end, n0, Bp, sBp)) return false;
+    m0 = uniform_i64(m0);
+    m_end = uniform_i64(m_end);
+    n0 = uniform_i64(n0);
+    Bp = uniform_ptr(Bp);
+    sBp = uniform_ptr(sBp);
+    rows_m = (int)(m_end - m0 < BM ? m_end - m0 : BM);
+    rows_n = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+    rsrc_x = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + m0 * p.lda), (short)0, rows_m * (int)p.lda,
+                                               (int)kRsrcWord3);
+    rsrc_w = __builtin_amdgcn_make_buffer_rsrc((void*)(Bp + n0 * p.ldb), (short)0, rows_n * (int)p.ldb,
+                                               (int)kRsrcWord3);
+    rsrc_sw = __builtin_amdgcn_make_buffer_rsrc((void*)sBp, (short)0, (int)(sw_elems * 4), (int)kRsrcWord3);
+    const int64_t nbw = (n0 + 64 * wave) / 128;
+    sw_off = kLayout == kFprop ? (uint32_t)(nbw * p.ld_sb) * 4u : (uint32_t)nbw * 4u;
+    return true;
+  };
+  int64_t tile = blockIdx.x;
+  while (tile < tile_ids && !setup_tile(tile)) tile += gridDim.x;
+  if (tile >= tile_ids) return;
 
   auto issue_load = [&](int kb, int op, uint8_t* st, v8i (&wr)[DNI]) {
     if (op < 4) {
@@ -560,10 +596,6 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   const int x_hi = lrow * 128 + (((4 + lgrp) ^ sw) << 4);
 
   v4f acc[DNI][DNJ];
-#pragma unroll
-  for (int i = 0; i < DNI; ++i)
-#pragma unroll
-    for (int j = 0; j < DNJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   v8i w0[DNI], w1[DNI], w2[DNI], w3[DNI];
 
   // ---- one K block per step: token tile in stage st, weights in wc ----
@@ -587,8 +619,15 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   float wn = 1.f;                   // block kb+1: weight-side block scale
   v4f Pl[DNI];                      // last row of partial sums of block kb-1
   float cl = 0.f;                   // and its scale
+  auto zero_state = [&]() {
 #pragma unroll
-  for (int i = 0; i < DNI; ++i) Pl[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < DNI; ++i) {
+#pragma unroll
+      for (int j = 0; j < DNJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      Pl[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    cl = 0.f;
+  };
 
   auto prefetch = [&](const uint8_t* stn) {
     const float* sxl = reinterpret_cast<const float*>(stn + kDScaleOff);
@@ -691,13 +730,14 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     }
   };
 
-  // Prologue, in the steady-state order (weights of block 0; tile of block 0
-  // and weights of block 1; tile of block 1 and weights of block 2), blocks
-  // past K repeating the last block; then block 0's first operands.  Whole
-  // rounds of four steps follow with no conditions inside; when K is not a
-  // multiple of four blocks the last round pads with steps that fold with
-  // scale 0.
-  {
+  // Prologue of a tile, in the steady-state order (weights of block 0; tile
+  // of block 0 and weights of block 1; tile of block 1 and weights of block
+  // 2), blocks past K repeating the last block.  Its wait allows the 22 loads
+  // issued after block 0's tile (any stores issued after them are younger
+  // still), then block 0's first operands are read.  Whole rounds of four
+  // steps follow with no conditions inside; when K is not a multiple of four
+  // blocks the last round pads with steps that fold with scale 0.
+  auto issue_prologue = [&]() {
     auto clamp = [&](int b) { return b < KB ? b : KB - 1; };
 #pragma unroll
     for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(0, op, lds_s0, w0);
@@ -709,12 +749,15 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     for (int op = 0; op < kDDmaOps; ++op) issue_load(clamp(1), op, lds_s1, w1);
 #pragma unroll
     for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(2), op, lds_s2, w2);
-    wait_vm<kDDmaOps + 2 * kDWOps>();
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    prefetch(lds_s0);
-  }
+  };
+  zero_state();
+  issue_prologue();
+  for (;;) {
+  wait_vm<kDDmaOps + 2 * kDWOps>();
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  prefetch(lds_s0);
   using no_pad = std::integral_constant<bool, false>;
   using pad = std::integral_constant<bool, true>;
   const int KB4 = KB & ~3;
@@ -737,19 +780,27 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[i][DNJ - 1][v] = __builtin_fmaf(Pl[i][v], cl, acc[i][DNJ - 1][v]);
   }
-  // the last steps' reload DMA must land before the workgroup's LDS is released
+  // the last steps' reload DMA has landed and every wave is done with the
+  // stages before the next tile's DMA reuses them
   wait_vm_lgkm0<0>();
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  const int64_t em0 = m0, em_end = m_end, en0 = n0;
+  const int erows_m = rows_m, erows_n = rows_n;
+  int64_t next = tile + gridDim.x;
+  while (next < tile_ids && !setup_tile(next)) next += gridDim.x;
+  const bool more = next < tile_ids;
+  if (more) issue_prologue();
   // ---- epilogue: lane holds 4 consecutive n of row m for every (i, j) ----
-  if (rows_m == BM && rows_n == BN) {
-    // Full tile: the wave's 64 (n) x 128 (m) block goes through its own stage
-    // array (free once every wave has passed this barrier) so that every
-    // store instruction writes whole row segments of the output: 8 rows x
-    // 128 B (BF16) or 4 rows x 256 B (FP32, in two halves of 64 rows).  Lane
-    // stores of 4 values per row took ~2.5x as long, all workgroups of a round
-    // storing at once.  16-byte chunks are XOR-swizzled by row.
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    uint8_t* ob = wave == 0 ? lds_s0 : (wave == 1 ? lds_s1 : (wave == 2 ? lds_s2 : lds_s3));
+  if (erows_m == BM && erows_n == BN) {
+    // Full tile: the wave's 64 (n) x 128 (m) block goes through its own
+    // staging area so that every store instruction writes whole row segments
+    // of the output: 8 rows x 128 B (BF16) or 4 rows x 256 B (FP32, in two
+    // halves of 64 rows).  Lane stores of 4 values per row took ~2.5x as
+    // long, all workgroups of a round storing at once.  16-byte chunks are
+    // XOR-swizzled by row.
+    uint8_t* ob = lds_out[wave];
     if constexpr (!kOutF32) {
 #pragma unroll
       for (int j = 0; j < DNJ; ++j) {
@@ -770,7 +821,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
       for (int t = 0; t < BM / 8; ++t) {
         const int row = t * 8 + (lane >> 3), ch = lane & 7;
         const uint4 v = *reinterpret_cast<const uint4*>(ob + row * 128 + ((ch ^ (row & 7)) << 4));
-        uint16_t* dst = reinterpret_cast<uint16_t*>(p.C) + (m0 + row) * p.ldc + n0 + wave * 64 + ch * 8;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.C) + (em0 + row) * p.ldc + en0 + wave * 64 + ch * 8;
         *reinterpret_cast<uint4*>(dst) = v;
       }
     } else {
@@ -789,24 +840,47 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
         for (int t = 0; t < BM / 8; ++t) {
           const int row = t * 4 + (lane >> 4), ch = lane & 15;
           const float4 v = *reinterpret_cast<const float4*>(ob + row * 256 + ((ch ^ (row & 15)) << 4));
-          float* dst = reinterpret_cast<float*>(p.C) + (m0 + half * (BM / 2) + row) * p.ldc + n0 + wave * 64 + ch * 4;
+          float* dst = reinterpret_cast<float*>(p.C) + (em0 + half * (BM / 2) + row) * p.ldc + en0 + wave * 64 + ch * 4;
           *reinterpret_cast<float4*>(dst) = v;
         }
       }
     }
-    return;
-  }
+  } else {
 #pragma unroll
-  for (int j = 0; j < DNJ; ++j) {
-    const int64_t m = m0 + j * 16 + lrow;
-    if (m >= m_end) continue;
+    for (int j = 0; j < DNJ; ++j) {
+      const int64_t m = em0 + j * 16 + lrow;
+      if (m >= em_end) continue;
 #pragma unroll
-    for (int i = 0; i < DNI; ++i) {
-      const int64_t n = n0 + wave * 64 + i * 16 + lgrp * 4;
-      if (n >= p.N) continue;
-      store4<kOutF32>(p, m, n, acc[i][j]);
+      for (int i = 0; i < DNI; ++i) {
+        const int64_t n = en0 + wave * 64 + i * 16 + lgrp * 4;
+        if (n >= p.N) continue;
+        store4<kOutF32>(p, m, n, acc[i][j]);
+      }
     }
   }
+  if (!more) break;
+  tile = next;
+  zero_state();
+  }
+}
+
+// Compute units of the current device (cached); 0 if unknown.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 template <int kLayout, bool kGrouped>
@@ -820,21 +894,26 @@ hipError_t launch_typed(const GemmProblem& p, hipStream_t stream, int64_t grid, 
                          dim3(kThreads), 0, stream, p, total);
     }
   } else {
+    // persistent: one workgroup per CU (the LDS footprint allows no second
+    // one), a multiple of 8 so each workgroup stays on one XCD's tile run
+    const int64_t ids = grid;
+    const int cus = device_cus();
+    if (cus >= 8 && grid > cus) grid = cus / 8 * 8;
     if (p.b_tiled) {
       if (p.out_fp32) {
         hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped, true>), dim3((unsigned)grid),
-                           dim3(kThreads), 0, stream, p, total);
+                           dim3(kThreads), 0, stream, p, total, ids);
       } else {
         hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped, true>), dim3((unsigned)grid),
-                           dim3(kThreads), 0, stream, p, total);
+                           dim3(kThreads), 0, stream, p, total, ids);
       }
     } else {
       if (p.out_fp32) {
         hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped, false>), dim3((unsigned)grid),
-                           dim3(kThreads), 0, stream, p, total);
+                           dim3(kThreads), 0, stream, p, total, ids);
       } else {
         hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped, false>), dim3((unsigned)grid),
-                           dim3(kThreads), 0, stream, p, total);
+                           dim3(kThreads), 0, stream, p, total, ids);
       }
     }
   }

@@ -328,8 +328,10 @@ static fp8_status validate_gemm_common(int64_t M, int64_t N, int64_t K, const ui
   if (M == 0) return FP8_OK;
   if (!A || !sA || !B || !sB || !C) return FP8_ERR_NULL;
   if (lda < K || ld_sa < M || ldc < N) return FP8_ERR_LD;
-  // the kernels address one 256-row tile with 32-bit byte offsets
+  // the kernels address one 256-row tile, and a scale table's K blocks, with
+  // 32-bit byte offsets
   if (lda > (int64_t{1} << 23)) return FP8_ERR_UNSUPPORTED;
+  if ((K / 128) * ld_sa * 4 >= (int64_t{1} << 31)) return FP8_ERR_UNSUPPORTED;
   const int64_t esz = c_dtype == FP8_OUT_FP32 ? 4 : 2;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C) || lda % 16 != 0 || (ldc * esz) % 16 != 0 ||
       !aligned4(sA) || !aligned4(sB))
@@ -365,9 +367,9 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
   if (tiled && ldb != K) return FP8_ERR_LD;       // dense tiles: the row "stride" is K
   if (ldb % 16 != 0) return FP8_ERR_ALIGN;
   if (ldb > (int64_t{1} << 23)) return FP8_ERR_UNSUPPORTED;
+  // the scale tables are read through buffers whose byte range is 32-bit
+  if (sb_rows * ld_sb * 4 >= (int64_t{1} << 31)) return FP8_ERR_UNSUPPORTED;
   if (layout == FP8_LAYOUT_DGRAD && K * ldb >= (int64_t{1} << 31)) return FP8_ERR_UNSUPPORTED;
-  // the weight-block scales are read through a buffer whose byte range is 32-bit
-  if (layout != FP8_LAYOUT_WGRAD && sb_rows * ld_sb >= (int64_t{1} << 29)) return FP8_ERR_UNSUPPORTED;
   const int64_t esz = c_dtype == FP8_OUT_FP32 ? 4 : 2;
   const Range rc = span(C, M, N * esz, ldc * esz);
   if (overlap(rc, span(A, M, K, lda)) || overlap(rc, span(B, b_rows, b_cols, ldb)) ||

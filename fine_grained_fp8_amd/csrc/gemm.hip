@@ -518,6 +518,9 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   int rows_m = 0, rows_n = 0;
   __amdgpu_buffer_rsrc_t rsrc_x, rsrc_w, rsrc_sw;
   uint32_t sw_off = 0;
+  const float* sa_tile = p.sA;      // token-side scales of the tile's rows, block 0
+  const float* sb_tile = p.sB;      // Wgrad: weight-side scales of the tile's columns, block 0
+  const uint32_t sa_kbytes = (uint32_t)p.ld_sa * 4u, sb_kbytes = (uint32_t)p.ld_sb * 4u;
   // token-side tile: rows m0.., DMA'd 8 rows x 128 B per instruction, 16-byte
   // chunks XOR-swizzled by row & 7 (row & 7 == (lane >> 3) & 7 here)
   const int xrow = wave * 32 + (lane >> 3);
@@ -555,6 +558,8 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     rsrc_sw = __builtin_amdgcn_make_buffer_rsrc((void*)sBp, (short)0, (int)(sw_elems * 4), (int)kRsrcWord3);
     const int64_t nbw = (n0 + 64 * wave) / 128;
     sw_off = kLayout == kFprop ? (uint32_t)(nbw * p.ld_sb) * 4u : (uint32_t)nbw * 4u;
+    sa_tile = p.sA + m0;
+    sb_tile = sBp + n0;
     return true;
   };
   int64_t tile = blockIdx.x;
@@ -566,13 +571,17 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_x, (lds_ptr_t)(st + (wave * 4 + op) * 1024), 16,
                                                off_x + (uint32_t)(kb * BK + op * 8 * (int)p.lda), 0, 0, 0);
     } else if (op == 4) {
+      // 32-bit block offset (validated: the scale tables stay below 2^31
+      // bytes) on a per-tile base keeps the resource cheap to rebuild
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.sA + (int64_t)kb * p.ld_sa + m0), (short)0, rows_m * 4, (int)kRsrcWord3);
+          (void*)(reinterpret_cast<const uint8_t*>(sa_tile) + (uint32_t)kb * sa_kbytes), (short)0, rows_m * 4,
+          (int)kRsrcWord3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + kDScaleOff), 16, (uint32_t)(lane * 16), 0, 0, 0);
     } else if (op == 5) {
       if constexpr (kLayout == kWgrad) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(sBp + (int64_t)kb * p.ld_sb + n0), (short)0, rows_n * 4, (int)kRsrcWord3);
+            (void*)(reinterpret_cast<const uint8_t*>(sb_tile) + (uint32_t)kb * sb_kbytes), (short)0, rows_n * 4,
+            (int)kRsrcWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + kDWScaleOff), 16, (uint32_t)(lane * 16), 0, 0, 0);
       } else {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_sw, (lds_ptr_t)(st + kDWScaleOff + wave * 256), 4,

@@ -224,6 +224,8 @@ fp8_status fp8_quant_weight_128x128_tiled(const void* w, int64_t rows, int64_t c
  *     become whole contiguous lines.
  *  C: [M][ldc >= N], BF16 (round to nearest even) or FP32 (c_dtype).
  *  M == 0 is a no-op.  C must not overlap A, B or the scales.
+ *  Limits (FP8_ERR_UNSUPPORTED beyond them): lda, ldb <= 2^23, and each
+ *  scale table (its rows x ld x 4 bytes) under 2 GiB.
  */
 fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t K,
                           const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,

@@ -137,6 +137,9 @@ def test_gemm_validation(lib):
     # WGRAD: any N, column scales [K/128][N]
     assert gemm(lib, layout=2, N=200, ldc=208, ld_sb=150) == LD
     assert gemm(lib, layout=2, N=200, ldc=208, ld_sb=200, dt=1) in (DEVICE, OK)
+    # scale tables of 2 GiB or more are not addressable with 32-bit offsets
+    assert gemm(lib, ld_sa=1 << 28) == UNSUP                  # 4 K blocks x 2^28 floats
+    assert gemm(lib, layout=2, ld_sb=1 << 28, dt=1) == UNSUP
 
 
 def test_quant_dual_validation(lib):

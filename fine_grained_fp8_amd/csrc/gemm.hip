@@ -567,9 +567,12 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   if (tile >= tile_ids) return;
 
   auto issue_load = [&](int kb, int op, uint8_t* st, v8i (&wr)[DNI]) {
+    // the per-step part of an address in the vector offset (one add per step,
+    // shared by the step's loads), the per-load constant in the scalar offset;
+    // the range check sees their sum, as before
     if (op < 4) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_x, (lds_ptr_t)(st + (wave * 4 + op) * 1024), 16,
-                                               off_x + (uint32_t)(kb * BK + op * 8 * (int)p.lda), 0, 0, 0);
+                                               off_x + (uint32_t)(kb * BK), (uint32_t)(op * 8 * (int)p.lda), 0, 0);
     } else if (op == 4) {
       // 32-bit block offset (validated: the scale tables stay below 2^31
       // bytes) on a per-tile base keeps the resource cheap to rebuild
@@ -590,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     } else {
       const int i = (op - 6) >> 1, h = (op - 6) & 1;
       const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
-          rsrc_w, off_w + (uint32_t)i * w_istride + (uint32_t)h * w_hstride + (uint32_t)kb * w_kstride, 0, 0);
+          rsrc_w, off_w + (uint32_t)kb * w_kstride, (uint32_t)i * w_istride + (uint32_t)h * w_hstride, 0);
       wr[i][4 * h + 0] = v[0];
       wr[i][4 * h + 1] = v[1];
       wr[i][4 * h + 2] = v[2];

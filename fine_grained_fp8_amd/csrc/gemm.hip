@@ -84,6 +84,11 @@ __device__ __forceinline__ void grouped_order(int64_t t, int64_t tiles_m, int64_
   tn = r / gsz;
 }
 
+__device__ __forceinline__ v8i join(const v4i& lo, const v4i& hi) {
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ v4i lo_half(const v8i& v) { return v4i{v[0], v[1], v[2], v[3]}; }
+__device__ __forceinline__ v4i hi_half(const v8i& v) { return v4i{v[4], v[5], v[6], v[7]}; }
 __device__ __forceinline__ v8i pair(const uint8_t* lo_p, const uint8_t* hi_p) {
   const v4i lo = *reinterpret_cast<const v4i*>(lo_p);
   const v4i hi = *reinterpret_cast<const v4i*>(hi_p);
@@ -658,12 +663,9 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     const int kb_d = kb + 2 < KB ? kb + 2 : KB - 1;   // token tile streamed this step
     const int kb_w = kb + 3 < KB ? kb + 3 : KB - 1;   // weights streamed this step
 
+    // c[j] (this block's scale of token subtile j) is formed in row j and
+    // first used in row j+1
     float c[DNJ];
-#pragma unroll
-    for (int j = 0; j < DNJ; ++j) {
-      const float t = kBlockW ? tn[j] * wn : tn[j];
-      c[j] = live ? t : 0.f;
-    }
     float4 rs[DNI];
     if constexpr (kLayout == kWgrad) {
       const float* swl = reinterpret_cast<const float*>(st + kDWScaleOff);
@@ -683,12 +685,20 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
       }
     };
 
-    v8i bx[DNJ];
-    bx[0] = bxa;
-    bx[1] = bxb;
+    v4i bxl[DNJ], bxh[DNJ];           // token-side operand halves, read two rows ahead
+    bxl[0] = lo_half(bxa); bxh[0] = hi_half(bxa);
+    bxl[1] = lo_half(bxb); bxh[1] = hi_half(bxb);
+    const float* sxn = reinterpret_cast<const float*>(stn + kDScaleOff);
+    const float* swn = reinterpret_cast<const float*>(stn + kDWScaleOff);
+    v4i an_l, an_h, bn_l, bn_h;       // block kb+1's first two operand rows
     // rows j of 4 MFMAs (the wave's 4 weight subtiles against token subtile
     // j), each MFMA followed by the fold of the same subtile's partial from
-    // row j-1 (row 0: the previous block's last row); two loads per row
+    // row j-1 (row 0: the previous block's last row).  The other work of a
+    // row is spread one item per MFMA so that no gap between two MFMAs holds
+    // more than the 28 issue cycles the matrix unit is busy: rows 0-5 read
+    // the operand halves of row j+2 (MFMAs 0 and 2) and issue two loads
+    // (MFMAs 1 and 3); row 5 ends with the wait and barrier for block kb+1,
+    // whose operands and scales rows 6-7 read.
     v4f P0[DNI], P1[DNI];
     // the operands stay in whichever register file the allocator gave them
     // (the MFMA reads both); pinning them to AGPRs costs a copy per register
@@ -697,20 +707,45 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     for (int j = 0; j < DNJ; ++j) {
       v4f (&Pc)[DNI] = (j & 1) ? P1 : P0;
       v4f (&Pp)[DNI] = (j & 1) ? P0 : P1;
-      if (j + 2 < DNJ) bx[j + 2] = pair(st + x_lo + (j + 2) * 2048, st + x_hi + (j + 2) * 2048);
+      const v8i bj = join(bxl[j], bxh[j]);
 #pragma unroll
       for (int i = 0; i < DNI; ++i) {
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
-        Pc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wc[i], bx[j], zero, 0, 0, 0, 127, 0, 127);
+        Pc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wc[i], bj, zero, 0, 0, 0, 127, 0, 127);
         if (j > 0) fold(acc[i][j - 1], Pp[i], c[j - 1], i);
         else if constexpr (kBlockW) fold(acc[i][DNJ - 1], Pl[i], cl, i);
+        if (i == 1) {
+          const float t = kBlockW ? tn[j] * wn : tn[j];
+          c[j] = live ? t : 0.f;
+        }
+        if (j + 2 < DNJ) {
+          if (i == 0) bxl[j + 2] = *reinterpret_cast<const v4i*>(st + x_lo + (j + 2) * 2048);
+          if (i == 2) bxh[j + 2] = *reinterpret_cast<const v4i*>(st + x_hi + (j + 2) * 2048);
+        }
+        if (j < kDOpsPerBlock / 2 && (i & 1)) {
+          const int op = 2 * j + (i >> 1);
+          issue_load(op < kDDmaOps ? kb_d : kb_w, op, sd, wf);
+        }
+        if (j == DNJ - 2) {
+          if (i == 0) an_l = *reinterpret_cast<const v4i*>(stn + x_lo);
+          if (i == 1) an_h = *reinterpret_cast<const v4i*>(stn + x_hi);
+          if (i == 2) bn_l = *reinterpret_cast<const v4i*>(stn + x_lo + 2048);
+          if (i == 3) bn_h = *reinterpret_cast<const v4i*>(stn + x_hi + 2048);
+        }
+        if (j == DNJ - 1) {
+          // the next block's scales; tn[0..7] are consumed by this step's
+          // rows before these reads (c[j] above), so they can be refilled
+          if (i == 0) { tn[0] = sxn[lrow]; tn[1] = sxn[16 + lrow]; }
+          if (i == 1) { tn[2] = sxn[32 + lrow]; tn[3] = sxn[48 + lrow]; }
+          if (i == 2) {
+            tn[4] = sxn[64 + lrow]; tn[5] = sxn[80 + lrow];
+            if constexpr (kBlockW) wn = swn[wave * 64];
+          }
+          if (i == 3) { tn[6] = sxn[96 + lrow]; tn[7] = sxn[112 + lrow]; }
+        }
         // instruction order = source order: one MFMA, then the fold of the
         // partial it produced four MFMAs (20 instructions) earlier
         __builtin_amdgcn_sched_barrier(0);
-      }
-      if (j < kDOpsPerBlock / 2) {
-        issue_load(2 * j < kDDmaOps ? kb_d : kb_w, 2 * j, sd, wf);
-        issue_load(2 * j + 1 < kDDmaOps ? kb_d : kb_w, 2 * j + 1, sd, wf);
       }
       if (j == kMid) {
         __builtin_amdgcn_sched_barrier(0);
@@ -719,9 +754,10 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
         __builtin_amdgcn_s_barrier();
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        prefetch(stn);
       }
     }
+    bxa = join(an_l, an_h);
+    bxb = join(bn_l, bn_h);
     if constexpr (kBlockW) {
 #pragma unroll
       for (int i = 0; i < DNI; ++i) Pl[i] = ((DNJ - 1) & 1) ? P1[i] : P0[i];
@@ -729,16 +765,6 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     } else {
 #pragma unroll
       for (int i = 0; i < DNI; ++i) fold(acc[i][DNJ - 1], ((DNJ - 1) & 1) ? P1[i] : P0[i], c[DNJ - 1], i);
-    }
-#pragma unroll
-    for (int j = 0; j < DNJ; ++j) {
-#pragma unroll
-      for (int i = 0; i < DNI; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (j > 0 || kBlockW) __builtin_amdgcn_sched_group_barrier(0x002, kLayout == kWgrad ? 8 : 4, 0);
-        if (i == 0 && j + 2 < DNJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        if ((i & 1) && j < kDOpsPerBlock / 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
     }
   };
 

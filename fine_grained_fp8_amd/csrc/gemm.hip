@@ -712,6 +712,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
       for (int i = 0; i < DNI; ++i) {
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
         Pc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wc[i], bj, zero, 0, 0, 0, 127, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
         if (j > 0) fold(acc[i][j - 1], Pp[i], c[j - 1], i);
         else if constexpr (kBlockW) fold(acc[i][DNJ - 1], Pl[i], cl, i);
         if (i == 1) {

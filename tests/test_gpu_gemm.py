@@ -75,6 +75,31 @@ def test_fprop_small(gpu_lib, case):
         check_gemm(bf16_bits(C), R, T, Xq.shape[1], out=out, E=E, label=case)
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_many_tiles_per_workgroup_ragged(gpu_lib, out_dtype):
+    """More tiles than CUs, so each persistent workgroup walks several (the
+    next tile's loads issued before the current tile's stores), with ragged
+    last rows and columns: full tiles take the staged epilogue, edge tiles the
+    lane-by-lane stores.  Every output is checked against the oracle, and the
+    operand-tiled run must match the row-major one bit for bit."""
+    xb = syn.activation_with_outliers(4168, 256, seed=81)       # 33 row tiles, last 72 rows
+    wb = syn.gaussian((2432, 256), seed=82, std=0.02)            # 9.5 column tiles of 256
+    Xq, sX = quant.quant_rows(xb)
+    Wq, sW = quant.quant_weight(wb)
+    R, T = og.fprop(Xq, sX, Wq, sW, with_magnitude=True)
+    E = truncation_bound(Xq, sX, Wq, og.expand_block_scales(sW, Wq.shape[0]))
+    C = run_fprop(gpu_lib, Xq, sX, Wq, sW, out_dtype)
+    if out_dtype == torch.float32:
+        check_gemm(C.cpu().numpy(), R, T, 256, out="fp32", E=E, label="330 tiles fp32")
+    else:
+        check_gemm(bf16_bits(C), R, T, 256, E=E, label="330 tiles bf16")
+    qt, st, _ = gpu_lib.quant_weight_128x128(dev(wb), tiled=True)
+    Ct = gpu_lib.block_gemm("fprop_tiled", dev(Xq), act_scales_dev(sX), qt, st, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    view = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(C.view(view), Ct.view(view))
+
+
 @pytest.fixture(scope="module")
 def big_layer():
     """Oracle-quantized X (4096 x 7168, outliers) and W (18432 x 7168)."""

@@ -412,9 +412,20 @@ def main():
         it = iter(range(1 << 30))
         batch["quantizer"] = batch_ms(lambda: fp8.quant_act_1x128(xs[next(it) & 3], "row"), 20)
         del xs
+    probe = None
     if want("fprop"):
         q3, s3, _ = fp8.quant_act_1x128(d["x3"], "row")
         batch["fprop.gemm"] = batch_ms(lambda: fp8.block_gemm("fprop_tiled", q3, s3, d["wq3_tl"], d["ws3"]), 5)
+        # context for the roofline: the GEMM's MFMA alone in a loop, on the
+        # bench's own operand bytes (2 KB of weight codes, 2 KB of X codes),
+        # one workgroup of four waves per CU as in the GEMM
+        codes = torch.cat([d["wq3_tl"].reshape(-1)[:2048], q3.reshape(-1)[:2048]]).contiguous()
+        n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+        iters = 20000
+        t_probe = batch_ms(lambda: fp8.probe_mfma(codes, n_cu, iters), 5)
+        probe = {"TFLOP/s": n_cu * 4 * 8 * iters * 65536.0 / t_probe / 1e9, "ms": t_probe,
+                 "what": f"{n_cu} workgroups x 4 waves x 8 x {iters} v_mfma_scale_f32_16x16x128_f8f6f4, "
+                         "no memory traffic, operands from the bench's weight and X codes"}
     log("batches: " + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in batch.items()))
     log(f"timed {args.steps} steps: {steps_ms:.2f} ms on the GPU, {wall:.2f} s wall")
 
@@ -450,7 +461,9 @@ def main():
                     "algorithmic_flop_per_launch": F3, "ms_per_launch": tg,
                     "timing": f"mean over the {args.steps} timed steps, HIP events around each launch on the launch stream",
                     "ms_per_launch_back_to_back": batch["fprop.gemm"],
-                    "TFLOP/s_back_to_back": F3 / batch["fprop.gemm"] / 1e9}
+                    "TFLOP/s_back_to_back": F3 / batch["fprop.gemm"] / 1e9,
+                    "mfma_loop": probe,
+                    "frac_of_mfma_loop": achieved / probe["TFLOP/s"] if probe else None}
     if want("backward"):
         tdual, tg1 = tm.mean_ms("bwd.quant_dual"), tm.mean_ms("dgrad.gemm")
         tq3, tg2 = tm.mean_ms("wgrad.quant_x"), tm.mean_ms("wgrad.gemm")

@@ -259,6 +259,17 @@ fp8_status fp8_quant_act_tiles(const void* x, int64_t rows, int64_t cols, int64_
                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
+fp8_status fp8_probe_mfma(int64_t workgroups, int32_t iters, const uint8_t* codes, float* out,
+                          void* stream) {
+  if (workgroups < 1 || workgroups > (int64_t{1} << 20) || iters < 1) return FP8_ERR_SHAPE;
+  if (!codes || !out) return FP8_ERR_NULL;
+  if (!aligned16(codes) || !aligned4(out)) return FP8_ERR_ALIGN;
+  if (overlap(span(codes, 1, 4096, 0), span(out, 1, workgroups * 256 * 4, 0))) return FP8_ERR_ALIAS;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  return launched(fp8bs::launch_mfma_probe(workgroups, iters, codes, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
 fp8_status fp8_gemm_promotion(const uint8_t* A, int64_t M, int64_t K, int64_t lda, const uint8_t* B,
                               int64_t N, int64_t ldb, int64_t promote_k, float* C, int64_t ldc,
                               void* stream) {

@@ -50,6 +50,9 @@ hipError_t launch_gemm_promotion(const uint8_t* A, int64_t lda, const uint8_t* B
                                  int64_t M, int64_t N, int64_t K, int64_t promote_k, float* C,
                                  int64_t ldc, hipStream_t stream);
 
+hipError_t launch_mfma_probe(int64_t workgroups, int iters, const uint8_t* codes, float* out,
+                             hipStream_t stream);
+
 enum GemmLayout { kFprop = 0, kDgrad = 1, kWgrad = 2, kDgradT = 3 };
 
 struct GemmProblem {

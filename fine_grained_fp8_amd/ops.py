@@ -307,6 +307,20 @@ def gemm_promotion(A: torch.Tensor, B: torch.Tensor, promote_k: int, *, stream=N
     return C
 
 
+def probe_mfma(codes: torch.Tensor, workgroups: int, iters: int, *, stream=None):
+    """Measurement aid: `workgroups` x 4 waves each run 8 * iters independent
+    FP8 MFMAs (65,536 FLOP each) on operands taken from `codes` (4096 uint8
+    E4M3 codes: A from bytes 32 l.., B from 2048 + 32 l.. for lane l), with no
+    memory traffic.  Returns the per-lane checksums [workgroups * 256] float32."""
+    lib = _lib.load_library()
+    if codes.dtype != torch.uint8 or codes.numel() < 4096 or not codes.is_contiguous():
+        raise ValueError("codes: a contiguous uint8 tensor of at least 4096 elements")
+    out = torch.empty(workgroups * 256, dtype=torch.float32, device=codes.device)
+    st = lib.fp8_probe_mfma(workgroups, iters, _ptr(codes), _ptr(out), _stream(stream))
+    _lib.check("fp8_probe_mfma", st)
+    return out
+
+
 def quant_act_tiles(x: torch.Tensor, tile: int = 128, rank: int = 1, *, sat_count=None, stream=None):
     """1 x tile quantization of x [rows][cols] BF16 with the clip value at the
     rank-th largest |x| of each tile (rank 1: the max).  Returns

@@ -372,6 +372,27 @@ fp8_status fp8_unpack_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t s
 fp8_status fp8_dequant_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t stride, void* y,
                               int64_t ldy, void* stream);
 
+/*
+ * fp8_probe_mfma - measurement aid for the GEMMs' roofline, not a step of the
+ * method: each wave runs 8 independent accumulator chains of the GEMMs' FP8
+ * MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, block scales 2^0) for `iters`
+ * rounds with no memory traffic, so its duration gives the matrix-unit rate
+ * the chip sustains on the given operand bytes (the clock under load depends
+ * on the power the data draws).
+ *  workgroups  1..2^20 workgroups of 256 threads (four waves); each wave does
+ *              8 * iters MFMAs of 65,536 FLOP
+ *  iters       >= 1
+ *  codes       device, 4096 bytes of E4M3 codes: lane l of every wave takes
+ *              operand A from bytes [32 l, 32 l + 32) and B from
+ *              [2048 + 32 l, 2048 + 32 l + 32); 16-byte aligned
+ *  out         device, workgroups * 256 floats: per lane, the sum of its
+ *              accumulators (a checksum that keeps the work observable)
+ *  Errors: FP8_ERR_SHAPE, FP8_ERR_NULL, FP8_ERR_ALIGN, FP8_ERR_ALIAS,
+ *  FP8_ERR_DEVICE, FP8_ERR_LAUNCH.
+ */
+fp8_status fp8_probe_mfma(int64_t workgroups, int32_t iters, const uint8_t* codes, float* out,
+                          void* stream);
+
 /* Static string naming a status; never NULL. */
 const char* fp8_status_string(fp8_status s);
 

@@ -390,3 +390,15 @@ def test_tiled_wgrad_full_size_bit_identical(gpu_lib):
     b = gpu_lib.block_gemm("wgrad_tiled", qd, sd, qx_t, sx_t, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_probe_mfma_counts_its_work(gpu_lib):
+    """The rate probe runs 8 * iters MFMAs per wave: with every code 1.0 each
+    of a lane's 4 outputs per chain gains 128 per MFMA, so its checksum is
+    8 * 4 * 128 * iters; with zero codes it is 0."""
+    ones = torch.full((4096,), 0x38, dtype=torch.uint8, device="cuda")
+    out = gpu_lib.probe_mfma(ones, 3, 5)
+    zero = gpu_lib.probe_mfma(torch.zeros(4096, dtype=torch.uint8, device="cuda"), 2, 7)
+    torch.cuda.synchronize()
+    assert torch.all(out == 8 * 4 * 128 * 5).item()
+    assert torch.all(zero == 0).item()

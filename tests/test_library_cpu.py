@@ -232,6 +232,17 @@ def test_quant_tiles_validation(lib):
         assert f(tile=tile, rank=8) in (DEVICE, OK)
 
 
+def test_probe_mfma_validation(lib):
+    f = lambda wg=4, it=2, codes=A, out=C: lib.fp8_probe_mfma(wg, it, codes, out, None)
+    assert f(wg=0) == SHAPE
+    assert f(it=0) == SHAPE
+    assert f(codes=None) == NULL
+    assert f(out=None) == NULL
+    assert f(codes=A + 8) == ALIGN
+    assert f(out=A + 1024) == ALIAS
+    assert f() in (DEVICE, OK)
+
+
 def test_gemm_promotion_validation(lib):
     f = lambda A_=A, M=64, K=256, lda=256, B_=B, N=48, ldb=256, pk=128, C_=C, ldc=48: \
         lib.fp8_gemm_promotion(A_, M, K, lda, B_, N, ldb, pk, C_, ldc, None)

@@ -21,23 +21,25 @@
 //    stay at 2^0 because the method's FP32 scales are not powers of two.
 //  * The weight-side operand is the MFMA "A" (rows = output columns n) and the
 //    token-side operand the MFMA "B" (columns = output rows m): each lane owns
-//    4 consecutive n of one output row m (contiguous stores), and in
-//    Fprop/Dgrad one weight-block scale per wave and K block.
+//    4 consecutive n of one output row m, and in Fprop/Dgrad one weight-block
+//    scale per wave and K block.
 //  * Workgroup tile 256 (n) x 128 (m) x 128 (k): four wave64s, one per SIMD,
-//    each 128 x 64 with the full 512-register budget (accumulators in VGPRs,
-//    operands free to live in AGPRs).
-//  * Three LDS stages, each tile of each stage its own LDS object (so the
-//    compiler sees that the DMA into one stage never aliases reads of
-//    another): K blocks kb+1 and kb+2 stream in by DMA (buffer_load_dwordx4
-//    ... lds, no staging registers) while block kb is multiplied; one barrier
-//    per K block.  The buffer range ends at the last valid row, so ragged M/N
-//    tails read zeros.  Tiles store 16-byte chunks XOR-swizzled by row & 7
-//    (conflict-free MFMA operand reads).  The scales of each K block
-//    (contiguous in the MN-major layout) ride along in the same stage.
-//  * Dgrad reads the forward weight codes W_q [d_out][d_in] transposed: the
-//    tile is DMA'd as stored ([k][n]) and ds_read_b64_tr_b8 transposes it on
-//    the way into the MFMA operand registers.
-//  * Workgroup ids are remapped so each XCD (ids congruent mod 8) walks a
+//    with the full 512-register budget each.
+//  * block_gemm_direct_kernel (Fprop, Dgrad from W_q^T, Wgrad, grouped): each
+//    wave's 64 weight-side rows go straight from memory into registers, the
+//    shared token-side tile through four LDS stages by DMA; persistent over
+//    tiles; details at the kernel.
+//  * block_gemm_kernel (Dgrad reading W_q as stored): both tiles through
+//    three LDS stages by DMA (buffer_load_dwordx4 ... lds, no staging
+//    registers), each stage its own LDS object so the compiler sees that the
+//    DMA into one stage never aliases reads of another; waves 128 x 64; the
+//    weight tile is DMA'd as stored ([k][n]) and ds_read_b64_tr_b8 transposes
+//    it on the way into the MFMA operand registers.
+//  * Buffer ranges end at the last valid row, so ragged M/N tails read zeros.
+//    LDS tiles store 16-byte chunks XOR-swizzled by row & 7 (conflict-free
+//    operand reads).  The scales of each K block (contiguous in the MN-major
+//    layout) ride along in the same stage.
+//  * Tile ids are remapped so each XCD (ids congruent mod 8) walks a
 //    contiguous, M-grouped run of tiles and its private L2 sees the reuse.
 #include <atomic>
 #include <type_traits>
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
 
 
 // ---------------------------------------------------------------------------
-// Direct-weight kernel (Fprop, Wgrad, grouped Fprop).
+// Direct-weight kernel (Fprop, Dgrad from W_q^T, Wgrad, grouped Fprop).
 //
 // Each wave owns 64 output columns (n) x all 128 token rows (m) of the
 // 256 x 128 workgroup tile.  Its weight-side rows are private, so they skip
@@ -478,7 +480,9 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
 // layout, four K blocks deep.  Only the token-side tile, shared by the four
 // waves, goes through LDS (four stages, DMA).  Per K step and CU this moves
 // 80 KB through LDS (16 KB DMA writes + 64 KB operand reads) and 49 KB through
-// the vector-memory unit, both below the 32 MFMAs per wave of the step.
+// the vector-memory unit, both below the 32 MFMAs per wave of the step.  The
+// launch is persistent (one workgroup per CU walking its XCD's tiles) and
+// full tiles store whole output row segments through an LDS staging area.
 //
 // k order inside an operand register: lane group g (= lane / 16) holds bytes
 // 16g..16g+15 and 64+16g..64+16g+15 of the 128-byte K block (two aligned
@@ -486,7 +490,6 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
 // the MFMA contracts the same 128 products; each aligned run of 8 k stays
 // together inside the MFMA.
 // ---------------------------------------------------------------------------
-constexpr int kDS = 4;                         // LDS stages = weight register buffers
 constexpr int DNI = 4, DNJ = 8;                // wave tile: 64 (n) x 128 (m)
 constexpr int kDScaleOff = BM * BK;            // token-side scales (1 KB DMA footprint)
 constexpr int kDWScaleOff = kDScaleOff + 1024; // weight-side scales (1 KB)

@@ -22,11 +22,12 @@ from .ops import (  # noqa: F401
     gemm_promotion,
     quant_act_tiles,
     probe_mfma,
+    probe_recip_online,
     round_up,
 )
 
 __all__ = [
     "FP8Error", "load_library", "quant_act_1x128", "quant_act_dual", "quant_weight_128x128", "block_gemm",
     "block_gemm_grouped", "amax_history_update", "cast_e4m3", "message_bytes", "pack_tokens",
-    "unpack_tokens", "dequant_tokens", "gemm_promotion", "quant_act_tiles", "probe_mfma", "round_up",
+    "unpack_tokens", "dequant_tokens", "gemm_promotion", "quant_act_tiles", "probe_mfma", "probe_recip_online", "round_up",
 ]

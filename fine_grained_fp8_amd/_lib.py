@@ -45,6 +45,7 @@ SIGNATURES = {
     "fp8_quant_act_tiles": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _P, _I64, _P, _I64, _P, _P]),
     "fp8_gemm_promotion": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "fp8_probe_mfma": (ctypes.c_int, [_I64, ctypes.c_int32, _P, _P, _P]),
+    "fp8_probe_recip_online": (ctypes.c_int, [_P, _P, _I64, _P]),
     "fp8_pack_tokens": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "fp8_unpack_tokens": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "fp8_dequant_tokens": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P]),

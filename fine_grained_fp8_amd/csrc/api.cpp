@@ -270,6 +270,17 @@ fp8_status fp8_probe_mfma(int64_t workgroups, int32_t iters, const uint8_t* code
   return launched(fp8bs::launch_mfma_probe(workgroups, iters, codes, out, reinterpret_cast<hipStream_t>(stream)));
 }
 
+fp8_status fp8_probe_recip_online(const float* s, float* r, int64_t n, void* stream) {
+  if (n < 0 || n > (int64_t{1} << 30)) return FP8_ERR_SHAPE;
+  if (n == 0) return FP8_OK;
+  if (!s || !r) return FP8_ERR_NULL;
+  if (!aligned4(s) || !aligned4(r)) return FP8_ERR_ALIGN;
+  if (overlap(span(s, 1, n * 4, 0), span(r, 1, n * 4, 0))) return FP8_ERR_ALIAS;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  return launched(fp8bs::launch_recip_online_probe(s, r, n, reinterpret_cast<hipStream_t>(stream)));
+}
+
 fp8_status fp8_gemm_promotion(const uint8_t* A, int64_t M, int64_t K, int64_t lda, const uint8_t* B,
                               int64_t N, int64_t ldb, int64_t promote_k, float* C, int64_t ldc,
                               void* stream) {

@@ -58,13 +58,36 @@ __device__ __forceinline__ uint32_t absmax_bits8(uint4 d) {
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
+// fl32(a / 448) for a finite non-negative BF16 value a: one Newton-Markstein
+// correction of y = fl32(a * fl32(1/448)) (the remainder a - 448 y is exact
+// with an FMA).  Equal to the IEEE quotient for every such a: checked
+// exhaustively on the host (tests/c/check_div.c).  Three operations instead
+// of a full correctly rounded division.
+__device__ __forceinline__ float div448_bf16(float a) {
+  constexpr float r448 = 1.0f / 448.0f;
+  const float y = a * r448;
+  const float e = __builtin_fmaf(-y, 448.0f, a);
+  return __builtin_fmaf(e, r448, y);
+}
+
 // Online tile scale from the tile's |x| max bits: max(fl32(amax/448), floor);
-// a NaN in the tile gives the canonical NaN (fmaxf would drop it).
+// a NaN in the tile gives the canonical NaN (fmaxf would drop it), an
+// infinite max the infinite scale.
 __device__ __forceinline__ float tile_scale(uint32_t amax_bits) {
   if (amax_bits > kBf16InfAbs) return __uint_as_float(kCanonicalNaN);
-  float amax = __uint_as_float(amax_bits << 16);
-  float s = amax / 448.0f;               // IEEE division (correctly rounded)
-  return fmaxf(s, scale_floor());
+  if (amax_bits == kBf16InfAbs) return __uint_as_float(0x7F800000u);
+  return fmaxf(div448_bf16(__uint_as_float(amax_bits << 16)), scale_floor());
+}
+
+// fl32(1 / s) for a finite online scale s = tile_scale(amax): the hardware
+// reciprocal estimate refined by one Newton step through FMAs.  Equal to the
+// IEEE reciprocal for every scale the online rule can produce (all finite
+// BF16 maxima and the floor): checked exhaustively on the GPU
+// (fp8_probe_recip_online).
+__device__ __forceinline__ float recip_online(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, r0, 1.0f);
+  return __builtin_fmaf(e, r0, r0);
 }
 
 __device__ __forceinline__ float amax_value(uint32_t amax_bits) {

@@ -52,6 +52,7 @@ hipError_t launch_gemm_promotion(const uint8_t* A, int64_t lda, const uint8_t* B
 
 hipError_t launch_mfma_probe(int64_t workgroups, int iters, const uint8_t* codes, float* out,
                              hipStream_t stream);
+hipError_t launch_recip_online_probe(const float* s, float* r, int64_t n, hipStream_t stream);
 
 enum GemmLayout { kFprop = 0, kDgrad = 1, kWgrad = 2, kDgradT = 3 };
 

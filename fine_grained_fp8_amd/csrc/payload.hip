@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void pack_tokens_kernel(
       s = tile_scale(ta);
       const uint4 d = v[i];
       if (ta < kBf16InfAbs) {
-        const float r = 1.0f / s;
+        const float r = recip_online(s);
         out.x = pack4_sat(div_by_scale(bf16_lo(d.x), s, r), div_by_scale(bf16_hi(d.x), s, r),
                           div_by_scale(bf16_lo(d.y), s, r), div_by_scale(bf16_hi(d.y), s, r));
         out.y = pack4_sat(div_by_scale(bf16_lo(d.z), s, r), div_by_scale(bf16_hi(d.z), s, r),

@@ -39,4 +39,18 @@ hipError_t launch_mfma_probe(int64_t workgroups, int iters, const uint8_t* codes
   return hipGetLastError();
 }
 
+// The quantizers' reciprocal of an online scale, element by element (for the
+// exhaustive check that it equals the IEEE reciprocal on every such scale).
+__global__ __launch_bounds__(256) void recip_online_probe_kernel(const float* __restrict__ s,
+                                                                 float* __restrict__ r, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) r[i] = recip_online(s[i]);
+}
+
+hipError_t launch_recip_online_probe(const float* s, float* r, int64_t n, hipStream_t stream) {
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(recip_online_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, s, r, n);
+  return hipGetLastError();
+}
+
 }  // namespace fp8bs

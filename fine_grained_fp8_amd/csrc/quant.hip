@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint4 d = v[g];
     uint2 out;
     if (!kExternal && t < kBf16InfAbs) {
-      const float r = 1.0f / s;              // correctly rounded reciprocal
+      const float r = recip_online(s);       // correctly rounded reciprocal
       out.x = pack4_sat(div_by_scale(bf16_lo(d.x), s, r), div_by_scale(bf16_hi(d.x), s, r),
                         div_by_scale(bf16_lo(d.y), s, r), div_by_scale(bf16_hi(d.y), s, r));
       out.y = pack4_sat(div_by_scale(bf16_lo(d.z), s, r), div_by_scale(bf16_hi(d.z), s, r),
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
       for (int i = 0; i < 16; ++i) y[i] = h ? bf16_hi(d[i]) : bf16_lo(d[i]);
       uint4 out;
       if (tt < kBf16InfAbs) {
-        const float r = 1.0f / s;
+        const float r = recip_online(s);
 #pragma unroll
         for (int i = 0; i < 16; ++i) y[i] = div_by_scale(y[i], s, r);
         out.x = pack4_sat(y[0], y[1], y[2], y[3]);
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
       const uint4 d = v[i];
       uint2 out;
       if (ta < kBf16InfAbs) {
-        const float r = 1.0f / s;
+        const float r = recip_online(s);
         out.x = pack4_sat(div_by_scale(bf16_lo(d.x), s, r), div_by_scale(bf16_hi(d.x), s, r),
                           div_by_scale(bf16_lo(d.y), s, r), div_by_scale(bf16_hi(d.y), s, r));
         out.y = pack4_sat(div_by_scale(bf16_lo(d.z), s, r), div_by_scale(bf16_hi(d.z), s, r),
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
         const float s = tile_scale(tt);
         uint32_t w[4];
         if (tt < kBf16InfAbs) {
-          const float r = 1.0f / s;
+          const float r = recip_online(s);
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             float y[4];
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
   const float s = tile_scale(m);
   if (t == 0) scales[bi * ld_s + bj] = s;
   const bool fast = m < kBf16InfAbs;
-  const float r = fast ? 1.0f / s : 0.0f;
+  const float r = fast ? recip_online(s) : 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int ci = t + 256 * i;

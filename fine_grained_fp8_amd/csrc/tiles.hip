@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void quant_tiles_kernel(
       const uint32_t w[4] = {d[h].x, d[h].y, d[h].z, d[h].w};
       float y[8];
       if (top0 < kBf16InfAbs) {
-        const float r = 1.0f / s;
+        const float r = recip_online(s);
         if (absmax_bits8(d[h]) <= ckey) {
           // every |x| <= c: the verified reciprocal shortcut
 #pragma unroll

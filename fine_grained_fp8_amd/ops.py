@@ -321,6 +321,18 @@ def probe_mfma(codes: torch.Tensor, workgroups: int, iters: int, *, stream=None)
     return out
 
 
+def probe_recip_online(s: torch.Tensor, *, stream=None):
+    """Verification aid: the quantizers' reciprocal of each online scale in s
+    (float32 device tensor); returns r of the same shape."""
+    lib = _lib.load_library()
+    if s.dtype != torch.float32 or not s.is_contiguous():
+        raise ValueError("s: a contiguous float32 tensor")
+    r = torch.empty_like(s)
+    st = lib.fp8_probe_recip_online(_ptr(s), _ptr(r), s.numel(), _stream(stream))
+    _lib.check("fp8_probe_recip_online", st)
+    return r
+
+
 def quant_act_tiles(x: torch.Tensor, tile: int = 128, rank: int = 1, *, sat_count=None, stream=None):
     """1 x tile quantization of x [rows][cols] BF16 with the clip value at the
     rank-th largest |x| of each tile (rank 1: the max).  Returns

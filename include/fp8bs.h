@@ -393,6 +393,17 @@ fp8_status fp8_dequant_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t 
 fp8_status fp8_probe_mfma(int64_t workgroups, int32_t iters, const uint8_t* codes, float* out,
                           void* stream);
 
+/*
+ * fp8_probe_recip_online - verification aid: r[i] = the reciprocal the
+ * quantizers use for an online scale s[i] (the hardware estimate refined by
+ * one Newton step through FMAs), so a test can check it against the IEEE
+ * reciprocal on every scale the online rule produces.
+ *  s, r   device, n floats each, 4-byte aligned, not overlapping; 0 <= n <= 2^30
+ *  Errors: FP8_ERR_SHAPE, FP8_ERR_NULL, FP8_ERR_ALIGN, FP8_ERR_ALIAS,
+ *  FP8_ERR_DEVICE, FP8_ERR_LAUNCH.
+ */
+fp8_status fp8_probe_recip_online(const float* s, float* r, int64_t n, void* stream);
+
 /* Static string naming a status; never NULL. */
 const char* fp8_status_string(fp8_status s);
 

@@ -9,7 +9,10 @@
  * finite non-negative BF16 tile max a, its scale s = max(fl32(a / 448),
  * fl32(1e-12)), and every BF16 x with |x| <= a (both signs).  Quotients below
  * 2^-11 in magnitude need only agree in sign (both encode to a zero code).
- * Exit status 0 = all pairs agree; prints the pair count.
+ * It also checks the scale's own division, fl32(a / 448) computed as one
+ * correction of y = fl32(a * fl32(1/448)), against the IEEE quotient for
+ * every finite non-negative BF16 a.
+ * Exit status 0 = all pairs and scales agree; prints the counts.
  */
 #include <math.h>
 #include <stdint.h>
@@ -49,5 +52,23 @@ int main(void) {
     }
   }
   printf("pairs=%llu mismatches=%llu\n", (unsigned long long)pairs, (unsigned long long)bad);
-  return bad != 0;
+
+  /* The scale itself: fl32(a / 448) through one correction of
+   * y = fl32(a * fl32(1/448)), for every finite non-negative BF16 a. */
+  const float r448 = 1.0f / 448.0f;
+  uint64_t scales = 0, bad_s = 0;
+  for (uint32_t ab = 0; ab <= 0x7F7Fu; ++ab) {
+    const float a = f(ab << 16);
+    const volatile float ref = a / 448.0f;
+    const float y = a * r448;
+    const float e = fmaf(-y, 448.0f, a);
+    const float q = fmaf(e, r448, y);
+    ++scales;
+    if (u(q) != u(ref)) {
+      if (bad_s < 10) printf("scale mismatch a=%08x q=%08x ref=%08x\n", u(a), u(q), u(ref));
+      ++bad_s;
+    }
+  }
+  printf("scales=%llu scale_mismatches=%llu\n", (unsigned long long)scales, (unsigned long long)bad_s);
+  return bad != 0 || bad_s != 0;
 }

@@ -292,3 +292,21 @@ def test_cast_exhaustive_all_fp32(gpu_lib):
         assert torch.equal(gotn, wantn), f"negative patterns from {start:#x}"
         del bits, x, want, got, neg, xn, wantn, gotn
     torch.cuda.synchronize()
+
+
+def test_online_reciprocal_exact_on_every_online_scale(gpu_lib):
+    """The quantizers take r = fl32(1/s) of an online scale from the hardware
+    reciprocal estimate refined by one FMA Newton step.  The division
+    shortcut's exhaustive host check assumes r is the IEEE reciprocal, so
+    this checks exactly that on every scale the online rule can produce:
+    s = max(fl32(a / 448), fl32(1e-12)) for every finite non-negative BF16 a
+    (the reference reciprocal is numpy's correctly rounded float32 division)."""
+    a = (np.arange(0, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    floor = np.array([0x2B8CBCCC], np.uint32).view(np.float32)[0]
+    s = np.unique(np.maximum(a / np.float32(448.0), floor)).astype(np.float32)
+    want = (np.float32(1.0) / s).astype(np.float32)
+    got = gpu_lib.probe_recip_online(torch.from_numpy(s).cuda())
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    bad = np.flatnonzero(got.view(np.uint32) != want.view(np.uint32))
+    assert bad.size == 0, [(float(s[i]), float(got[i]), float(want[i])) for i in bad[:5]]

@@ -232,6 +232,16 @@ def test_quant_tiles_validation(lib):
         assert f(tile=tile, rank=8) in (DEVICE, OK)
 
 
+def test_probe_recip_validation(lib):
+    f = lambda s=A, r=C, n=64: lib.fp8_probe_recip_online(s, r, n, None)
+    assert f(n=-1) == SHAPE
+    assert f(n=0, s=None) == OK
+    assert f(s=None) == NULL
+    assert f(r=A + 2) == ALIGN
+    assert f(r=A + 128) == ALIAS
+    assert f() in (DEVICE, OK)
+
+
 def test_probe_mfma_validation(lib):
     f = lambda wg=4, it=2, codes=A, out=C: lib.fp8_probe_mfma(wg, it, codes, out, None)
     assert f(wg=0) == SHAPE
@@ -332,3 +342,4 @@ def test_division_shortcut_exhaustive(tmp_path):
     assert res.returncode == 0, res.stdout
     assert "mismatches=0" in res.stdout
     assert "pairs=1065402240" in res.stdout
+    assert "scales=32640 scale_mismatches=0" in res.stdout

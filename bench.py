@@ -319,6 +319,8 @@ def main():
             tm.pending.append(("fprop", ev0, ev1))
             # the same GEMM reading row-major weight codes, for comparison
             tm.region("fprop_rowmajor.gemm", lambda: fp8.block_gemm("fprop", q, s, d["wq3"], d["ws3"]))
+            # the same product with the 1x128 quantization fused into the GEMM
+            tm.region("fprop_fused.gemm", lambda: fp8.block_gemm_fused_quant(d["x3"], d["wq3"], d["ws3"]))
         if want("backward"):
             ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
             # dY in both orientations from one read (Dgrad rows, Wgrad columns)
@@ -450,6 +452,12 @@ def main():
                          "ms_gemm_rowmajor_weights": trm, "TFLOP/s_gemm_rowmajor_weights": F3 / trm / 1e9,
                          "ms_gemm_median_p10_p90": tm.spread_ms("fprop.gemm"),
                          "ms_quant_plus_gemm_median_p10_p90": tm.spread_ms("fprop")}
+        tf = tm.mean_ms("fprop_fused.gemm")
+        rows["fprop_fused_quant"] = {
+            "ms": tf, "TFLOP/s": F3 / tf / 1e9,
+            "what": "BF16 X in, 1x128 quantization fused into a 128x128-tile GEMM (row-major weight codes)",
+            "unfused_ms_quant_plus_gemm_rowmajor": tq + trm, "unfused_ms_quant_plus_gemm_tiled": tq + tg,
+            "fused_over_unfused_tiled": tf / (tq + tg)}
         # the kernel's mean launch duration over the timed steps (HIP events
         # around each launch on its stream); the back-to-back batch after the
         # steps runs under sustained power and is reported beside it

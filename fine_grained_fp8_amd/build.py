@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfp8bs.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "payload.hip", "accum.hip", "tiles.hip", "probe.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "payload.hip", "accum.hip", "tiles.hip", "probe.hip", "fused.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

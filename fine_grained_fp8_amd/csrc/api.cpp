@@ -411,6 +411,45 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
   return launched(fp8bs::launch_gemm(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
+fp8_status fp8_block_gemm_fused_quant(int64_t M, int64_t N, int64_t K, const void* x, int64_t ldx,
+                                     const uint8_t* W, int64_t ldw, const float* sW, int64_t ld_sw,
+                                     void* C, fp8_out_dtype c_dtype, int64_t ldc, uint8_t* q_out,
+                                     int64_t ldq, float* s_out, int64_t ld_s, void* stream) {
+  if (c_dtype != FP8_OUT_BF16 && c_dtype != FP8_OUT_FP32) return FP8_ERR_UNSUPPORTED;
+  if (M < 0 || N <= 0 || K <= 0 || K % 128 != 0 || N % 128 != 0) return FP8_ERR_SHAPE;
+  if (M == 0) return FP8_OK;
+  if (!x || !W || !sW || !C) return FP8_ERR_NULL;
+  if ((q_out == nullptr) != (s_out == nullptr)) return FP8_ERR_NULL;
+  if (ldx < K || ldw < K || ld_sw < K / 128 || ldc < N) return FP8_ERR_LD;
+  if (q_out && (ldq < K || ld_s < M)) return FP8_ERR_LD;
+  const int64_t esz = c_dtype == FP8_OUT_FP32 ? 4 : 2;
+  if (!aligned16(x) || ldx % 8 != 0 || !aligned16(W) || ldw % 16 != 0 || !aligned16(C) ||
+      (ldc * esz) % 16 != 0 || !aligned4(sW))
+    return FP8_ERR_ALIGN;
+  if (q_out && (!aligned16(q_out) || ldq % 16 != 0 || !aligned4(s_out))) return FP8_ERR_ALIGN;
+  // one 128-row tile of X or W, and the weight-scale row, within 32-bit byte offsets
+  if (ldx > (int64_t{1} << 22) || ldw > (int64_t{1} << 23)) return FP8_ERR_UNSUPPORTED;
+  const Range rc = span(C, M, N * esz, ldc * esz);
+  if (overlap(rc, span(x, M, K * 2, ldx * 2)) || overlap(rc, span(W, N, K, ldw)) ||
+      overlap(rc, span(sW, N / 128, (K / 128) * 4, ld_sw * 4)))
+    return FP8_ERR_ALIAS;
+  if (q_out) {
+    const Range rq = span(q_out, M, K, ldq), rs = span(s_out, K / 128, M * 4, ld_s * 4);
+    if (overlap(rq, rc) || overlap(rs, rc) || overlap(rq, rs) || overlap(rq, span(x, M, K * 2, ldx * 2)) ||
+        overlap(rs, span(x, M, K * 2, ldx * 2)))
+      return FP8_ERR_ALIAS;
+  }
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  fp8bs::FusedFpropProblem p{};
+  p.M = M; p.N = N; p.K = K;
+  p.X = static_cast<const uint16_t*>(x); p.ldx = ldx;
+  p.W = W; p.ldw = ldw; p.sW = sW; p.ld_sw = ld_sw;
+  p.C = C; p.ldc = ldc; p.out_fp32 = c_dtype == FP8_OUT_FP32;
+  p.q_out = q_out; p.ldq = ldq; p.s_out = s_out; p.ld_s = ld_s;
+  return launched(fp8bs::launch_fused_quant_fprop(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
 namespace {
 fp8_status grouped_impl(int32_t groups, const int32_t* offsets_dev, int64_t total_M, int64_t N,
                         int64_t K, const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,

@@ -78,4 +78,23 @@ struct GemmProblem {
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 
+// Fprop with the 1x128 quantization of X fused in (BF16 X in).
+struct FusedFpropProblem {
+  int64_t M, N, K;
+  const uint16_t* X;     // BF16 [M][ldx]
+  int64_t ldx;
+  const uint8_t* W;      // W_q [N][ldw]
+  int64_t ldw;
+  const float* sW;       // [N/128][ld_sw]
+  int64_t ld_sw;
+  void* C;
+  int64_t ldc;
+  int out_fp32;
+  uint8_t* q_out;        // optional: the codes [M][ldq] and scales [K/128][ld_s]
+  int64_t ldq;
+  float* s_out;
+  int64_t ld_s;
+};
+hipError_t launch_fused_quant_fprop(const FusedFpropProblem& p, hipStream_t stream);
+
 }  // namespace fp8bs

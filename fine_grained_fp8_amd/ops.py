@@ -175,6 +175,37 @@ def block_gemm(layout: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, 
     return out
 
 
+def block_gemm_fused_quant(x: torch.Tensor, W: torch.Tensor, sW: torch.Tensor, *, out_dtype=torch.bfloat16,
+                           with_codes: bool = False, out=None, stream=None):
+    """Fprop with the 1x128 quantization of X fused into the GEMM.
+
+    x: bfloat16 [M][K]; W: codes [N][K] (row-major); sW [N/128][>=K/128].
+    Returns C [M][N] (out_dtype), equal bit for bit to
+    block_gemm("fprop", *quant_act_1x128(x, "row")[:2], W, sW); with
+    with_codes=True returns (C, codes [M][K], scales [K/128][M_pad]) as the
+    kernel formed them.
+    """
+    lib = _lib.load_library()
+    _check_2d("x", x, _BF16)
+    _check_2d("W", W, (torch.uint8, torch.float8_e4m3fn))
+    _check_2d("sW", sW, (torch.float32,))
+    M, K = x.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    code = _lib.OUT_FP32 if out.dtype == torch.float32 else _lib.OUT_BF16
+    q = s = None
+    if with_codes:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        s = torch.empty((K // 128, round_up(M, 4)), dtype=torch.float32, device=x.device)
+    st = lib.fp8_block_gemm_fused_quant(
+        M, N, K, _ptr(x), x.stride(0), _ptr(W), W.stride(0), _ptr(sW), sW.stride(0), _ptr(out), code,
+        out.stride(0), _ptr(q) if q is not None else None, q.stride(0) if q is not None else 0,
+        _ptr(s) if s is not None else None, s.stride(0) if s is not None else 0, _stream(stream))
+    _lib.check("fp8_block_gemm_fused_quant", st)
+    return (out, q, s) if with_codes else out
+
+
 def block_gemm_grouped(offsets: torch.Tensor, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor,
                        sB: torch.Tensor, *, tiled: bool = False, out_dtype=torch.bfloat16, out=None,
                        stream=None):

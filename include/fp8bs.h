@@ -233,6 +233,28 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
                           void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream);
 
 /*
+ * fp8_block_gemm_fused_quant - FPROP with the 1x128 quantization of X fused
+ * into the GEMM ("Online Quantization During Training", section 5: fusing
+ * the scaling with its neighbours decides whether online scaling is
+ * affordable; "FP8 Mixed Precision: DeepSeek-V3 Training Architecture",
+ * section 3):  Y = fp8_block_gemm(FPROP, quant_1x128(X), W_q)  in one launch,
+ * the codes formed on chip by every output tile's workgroup.
+ *  x      BF16 X [M][ldx >= K], 16-byte aligned, ldx % 8 == 0, ldx <= 2^22.
+ *  W      W_q [N][ldw >= K] (row-major codes), sW [N/128][ld_sw >= K/128].
+ *  C      [M][ldc >= N], BF16 or FP32; bit-identical to fp8_quant_act_1x128
+ *         (ROW, online scales) followed by fp8_block_gemm (FPROP).
+ *  q_out, s_out  optional (both NULL or both set): the codes [M][ldq >= K]
+ *         and scales [K/128][ld_s >= M] the kernel formed, equal to
+ *         fp8_quant_act_1x128's outputs.
+ *  N % 128 == 0, K % 128 == 0.  M == 0 is a no-op.  C must not overlap the
+ *  inputs; q_out and s_out must not overlap C, X or each other.
+ */
+fp8_status fp8_block_gemm_fused_quant(int64_t M, int64_t N, int64_t K, const void* x, int64_t ldx,
+                                     const uint8_t* W, int64_t ldw, const float* sW, int64_t ld_sw,
+                                     void* C, fp8_out_dtype c_dtype, int64_t ldc, uint8_t* q_out,
+                                     int64_t ldq, float* s_out, int64_t ld_s, void* stream);
+
+/*
  * fp8_block_gemm_grouped - one launch of per-expert FPROP GEMMs over row
  * slices (one GPU's share of a mixture-of-experts FFN layer):
  *     for g in [0, groups): rows offsets[g] .. offsets[g+1]-1 of A and C use

@@ -142,6 +142,35 @@ def test_gemm_validation(lib):
     assert gemm(lib, layout=2, ld_sb=1 << 28, dt=1) == UNSUP
 
 
+def fused(lib, M=256, N=256, K=512, x=X, ldx=512, w=B, ldw=512, sw=S2, ld_sw=4, c=C, dt=0, ldc=256,
+          q=None, ldq=0, s=None, ld_s=0):
+    return lib.fp8_block_gemm_fused_quant(M, N, K, x, ldx, w, ldw, sw, ld_sw, c, dt, ldc, q, ldq, s, ld_s,
+                                          None)
+
+
+def test_fused_quant_gemm_validation(lib):
+    assert fused(lib, dt=5) == UNSUP
+    assert fused(lib, K=200, ldx=256, ldw=256) == SHAPE
+    assert fused(lib, N=200, ldc=256) == SHAPE
+    assert fused(lib, M=-1) == SHAPE
+    assert fused(lib, M=0, x=None) == OK
+    assert fused(lib, x=None) == NULL
+    assert fused(lib, q=Q, ldq=512) == NULL                   # codes without scales
+    assert fused(lib, ldx=256) == LD
+    assert fused(lib, ld_sw=2) == LD
+    assert fused(lib, q=Q, ldq=256, s=S, ld_s=256) == LD
+    assert fused(lib, q=Q, ldq=512, s=S, ld_s=100) == LD
+    assert fused(lib, ldx=516) == ALIGN                        # BF16 rows not 16-byte aligned
+    assert fused(lib, x=X + 8) == ALIGN
+    assert fused(lib, q=Q + 4, ldq=512, s=S, ld_s=256) == ALIGN
+    assert fused(lib, ldx=(1 << 22) + 8) == UNSUP
+    assert fused(lib, c=X + 4096) == ALIAS
+    assert fused(lib, q=C, ldq=512, s=S, ld_s=256) == ALIAS
+    assert fused(lib, q=Q, ldq=512, s=X + 1024, ld_s=256) == ALIAS
+    assert fused(lib) in (DEVICE, OK)
+    assert fused(lib, q=Q, ldq=512, s=S, ld_s=256, dt=1) in (DEVICE, OK)
+
+
 def test_quant_dual_validation(lib):
     f = lib.fp8_quant_act_dual
     base = dict(x=X, rows=256, cols=384, ldx=384, qr=A, ldqr=384, sr=S, ldsr=256, qc=B, ldqc=256,

@@ -1,5 +1,5 @@
 // Fprop with the 1x128 quantization of X fused into the GEMM: BF16 X in,
-// BF16/FP32 Y out, the codes never leave the chip.
+// BF16/FP32 Y out, the codes formed on chip (and optionally written out).
 //
 // Sources: "Online Quantization During Training" section 5 (whether online
 // scaling is affordable depends on fusing it with the neighbouring kernels;

@@ -97,6 +97,23 @@ class Timer:
         self.pending.append((name, ev0, ev1))
         return out
 
+    def chain(self, name, parts):
+        """Back-to-back launches bracketed by one event between each pair of
+        them: part i is timed between events i and i+1 and the whole region
+        between the first and the last, so the parts add up to the region
+        exactly."""
+        evs = [self.torch.cuda.Event(enable_timing=True)]
+        evs[0].record()
+        outs = []
+        for pname, fn in parts:
+            outs.append(fn(*outs[-1:]) if outs else fn())
+            ev = self.torch.cuda.Event(enable_timing=True)
+            ev.record()
+            self.pending.append((pname, evs[-1], ev))
+            evs.append(ev)
+        self.pending.append((name, evs[0], evs[-1]))
+        return outs
+
     def collect(self):
         self.torch.cuda.synchronize()
         for name, a, b in self.pending:
@@ -264,6 +281,10 @@ def main():
     if want("quantizer") or want("granularity"):
         d["x2"] = to_dev(syn.activation_with_outliers(8192, 7168, seed=0), torch)
     host = {}
+    if want("toy"):
+        xb1, wb1 = syn.toy_layer(0)
+        d["x1"] = to_dev(xb1, torch)
+        d["wq1_tl"], d["ws1"], _ = fp8.quant_weight_128x128(to_dev(wb1, torch), tiled=True)
     if want("fprop") or want("backward") or want("weights"):
         host["w3"] = syn.gaussian((18432, 7168), seed=1, std=0.02)
         d["w3"] = to_dev(host["w3"], torch)
@@ -311,12 +332,16 @@ def main():
     def step():
         if want("quantizer"):
             tm.region("quantizer", lambda: fp8.quant_act_1x128(d["x2"], "row"))
+        if want("toy"):
+            tm.chain("toy", [("toy.quant", lambda: fp8.quant_act_1x128(d["x1"], "row")),
+                             ("toy.gemm", lambda o: fp8.block_gemm("fprop_tiled", o[0], o[1], d["wq1_tl"],
+                                                                   d["ws1"]))])
         if want("fprop"):
-            ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
-            q, s, _ = tm.region("fprop.quant", lambda: fp8.quant_act_1x128(d["x3"], "row"))
-            tm.region("fprop.gemm", lambda: fp8.block_gemm("fprop_tiled", q, s, d["wq3_tl"], d["ws3"]))
-            ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
-            tm.pending.append(("fprop", ev0, ev1))
+            # the headline region: quantization of X, then the GEMM, with one
+            # event between them
+            (q, s, _), _ = tm.chain("fprop", [
+                ("fprop.quant", lambda: fp8.quant_act_1x128(d["x3"], "row")),
+                ("fprop.gemm", lambda o: fp8.block_gemm("fprop_tiled", o[0], o[1], d["wq3_tl"], d["ws3"]))])
             # the same GEMM reading row-major weight codes, for comparison
             tm.region("fprop_rowmajor.gemm", lambda: fp8.block_gemm("fprop", q, s, d["wq3"], d["ws3"]))
             # the same product with the 1x128 quantization fused into the GEMM
@@ -343,12 +368,10 @@ def main():
             tm.region("fwd.quant_dual_x", lambda: fp8.quant_act_dual(d["x3"], tiled=True))
             tm.region("fwd.quant_row_x", lambda: fp8.quant_act_1x128(d["x3"], "row"))
         if want("grouped"):
-            ev0 = torch.cuda.Event(enable_timing=True); ev0.record()
-            q, s, _ = tm.region("grouped.quant", lambda: fp8.quant_act_1x128(d["x5"], "row"))
-            tm.region("grouped.gemm", lambda: fp8.block_gemm_grouped(d["off5"], q, s, d["wq5_tl"], d["ws5"],
-                                                                     tiled=True))
-            ev1 = torch.cuda.Event(enable_timing=True); ev1.record()
-            tm.pending.append(("grouped", ev0, ev1))
+            (q, s, _), _ = tm.chain("grouped", [
+                ("grouped.quant", lambda: fp8.quant_act_1x128(d["x5"], "row")),
+                ("grouped.gemm", lambda o: fp8.block_gemm_grouped(d["off5"], o[0], o[1], d["wq5_tl"], d["ws5"],
+                                                                  tiled=True))])
             tm.region("grouped_rowmajor.gemm", lambda: fp8.block_gemm_grouped(d["off5"], q, s, d["wq5"], d["ws5"]))
         if want("granularity"):
             for T in (32, 64, 128, 256, 512, 1024):
@@ -415,7 +438,16 @@ def main():
         batch["quantizer"] = batch_ms(lambda: fp8.quant_act_1x128(xs[next(it) & 3], "row"), 20)
         del xs
     probe = None
+
+    def quant_then_gemm(x, w, sw):
+        q, s, _ = fp8.quant_act_1x128(x, "row")
+        return fp8.block_gemm("fprop_tiled", q, s, w, sw)
+
+    if want("toy"):
+        batch["toy.pair"] = batch_ms(lambda: quant_then_gemm(d["x1"], d["wq1_tl"], d["ws1"]), 200)
     if want("fprop"):
+        # the headline pair back to back with no event between the two launches
+        batch["fprop.pair"] = batch_ms(lambda: quant_then_gemm(d["x3"], d["wq3_tl"], d["ws3"]), 10)
         q3, s3, _ = fp8.quant_act_1x128(d["x3"], "row")
         batch["fprop.gemm"] = batch_ms(lambda: fp8.block_gemm("fprop_tiled", q3, s3, d["wq3_tl"], d["ws3"]), 5)
         # context for the roofline: the GEMM's MFMA alone in a loop, on the
@@ -424,10 +456,14 @@ def main():
         codes = torch.cat([d["wq3_tl"].reshape(-1)[:2048], q3.reshape(-1)[:2048]]).contiguous()
         n_cu = torch.cuda.get_device_properties(0).multi_processor_count
         iters = 20000
-        t_probe = batch_ms(lambda: fp8.probe_mfma(codes, n_cu, iters), 5)
-        probe = {"TFLOP/s": n_cu * 4 * 8 * iters * 65536.0 / t_probe / 1e9, "ms": t_probe,
-                 "what": f"{n_cu} workgroups x 4 waves x 8 x {iters} v_mfma_scale_f32_16x16x128_f8f6f4, "
-                         "no memory traffic, operands from the bench's weight and X codes"}
+        probe = {"what": f"{n_cu} workgroups x 4 waves x 8 x {iters} FP8 16x16x128 MFMAs, no memory "
+                         "traffic, operands from the bench's weight and X codes; plain = the GEMMs' "
+                         "v_mfma_f32_16x16x128_f8f6f4, scaled = its block-scaled encoding, fold = plain "
+                         "+ the 4 FP32 fold FMAs per MFMA (the GEMMs' per-block mix)"}
+        for mode in ("plain", "scaled", "fold"):
+            t_probe = batch_ms(lambda: fp8.probe_mfma(codes, n_cu, iters, mode), 5)
+            probe[mode] = {"TFLOP/s": n_cu * 4 * 8 * iters * 65536.0 / t_probe / 1e9, "ms": t_probe}
+        probe["TFLOP/s"] = probe["fold"]["TFLOP/s"]
     log("batches: " + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in batch.items()))
     log(f"timed {args.steps} steps: {steps_ms:.2f} ms on the GPU, {wall:.2f} s wall")
 
@@ -443,10 +479,16 @@ def main():
     roofline = None
     if want("fprop"):
         tq, tg, tt = tm.mean_ms("fprop.quant"), tm.mean_ms("fprop.gemm"), tm.mean_ms("fprop")
-        value = F3 / (tq + tg) / 1e9
+        # the headline: 2MNK over the timed region (quantization + GEMM back
+        # to back on one stream; its two parts add up to it exactly)
+        value = F3 / tt / 1e9
         trm = tm.mean_ms("fprop_rowmajor.gemm")
         rows["fprop"] = {"ms_quant": tq, "ms_gemm": tg, "ms_region": tt,
                          "TFLOP/s_incl_quant": value, "TFLOP/s_gemm": F3 / tg / 1e9,
+                         "what": "1x128 quantization kernel then the GEMM kernel, back to back on one stream "
+                                 "(the unfused pair; the fused kernel is the row fprop_fused_quant)",
+                         "ms_pair_back_to_back": batch["fprop.pair"],
+                         "TFLOP/s_pair_back_to_back": F3 / batch["fprop.pair"] / 1e9,
                          "quant_GB/s": 4096 * 7168 * (3 + 4 / 128) / tq / 1e6,
                          "weights": "operand-tiled codes",
                          "ms_gemm_rowmajor_weights": trm, "TFLOP/s_gemm_rowmajor_weights": F3 / trm / 1e9,
@@ -472,6 +514,15 @@ def main():
                     "TFLOP/s_back_to_back": F3 / batch["fprop.gemm"] / 1e9,
                     "mfma_loop": probe,
                     "frac_of_mfma_loop": achieved / probe["TFLOP/s"] if probe else None}
+    if want("toy"):
+        F1 = 2.0 * 128 * 256 * 128
+        rows["toy"] = {"what": "toy layer y = W x: 1x128 quantization of X 128x128, then the GEMM against "
+                               "W 256x128 (pre-quantized, operand-tiled codes), BF16 out",
+                       "us_region": tm.mean_ms("toy") * 1e3, "us_quant": tm.mean_ms("toy.quant") * 1e3,
+                       "us_gemm": tm.mean_ms("toy.gemm") * 1e3,
+                       "us_pair_back_to_back": batch["toy.pair"] * 1e3,
+                       "region_median_p10_p90_us": [v * 1e3 for v in tm.spread_ms("toy")],
+                       "flop": F1}
     if want("backward"):
         tdual, tg1 = tm.mean_ms("bwd.quant_dual"), tm.mean_ms("dgrad.gemm")
         tq3, tg2 = tm.mean_ms("wgrad.quant_x"), tm.mean_ms("wgrad.gemm")
@@ -504,7 +555,8 @@ def main():
         F5 = 2.0 * 16384 * 2048 * 7168
         tq, tg = tm.mean_ms("grouped.quant"), tm.mean_ms("grouped.gemm")
         tgr = tm.mean_ms("grouped_rowmajor.gemm")
-        rows["grouped"] = {"ms_quant": tq, "ms_gemm": tg, "TFLOP/s_incl_quant": F5 / (tq + tg) / 1e9,
+        rows["grouped"] = {"ms_quant": tq, "ms_gemm": tg, "ms_region": tm.mean_ms("grouped"),
+                           "TFLOP/s_incl_quant": F5 / tm.mean_ms("grouped") / 1e9,
                            "TFLOP/s_gemm": F5 / tg / 1e9, "tokens_per_expert": [int(c) for c in d["counts5"]],
                            "weights": "operand-tiled codes",
                            "ms_gemm_rowmajor_weights": tgr, "TFLOP/s_gemm_rowmajor_weights": F5 / tgr / 1e9}

@@ -7,7 +7,7 @@
 // Architecture" section 3 (partial products accumulated in FP32 registers).
 //
 // C[m][n] = sum_k A[m][k] B[n][k] over E4M3 codes (unit scales), FP32 out.
-//  - promote_k a multiple of 128: one v_mfma_scale_f32_16x16x128_f8f6f4 per
+//  - promote_k a multiple of 128: one v_mfma_f32_16x16x128_f8f6f4 per
 //    128-wide K block with the MFMA accumulator carried from block to block
 //    (the MFMA's C input) for promote_k / 128 blocks, then added to the FP32
 //    running sum and cleared.  promote_k = 128 is the method's interval and
@@ -20,6 +20,7 @@
 // memory in the byte order of the block GEMM's direct kernel (lane group g:
 // bytes 16g.. and 64+16g.. of the K block), so the MFMA sees the same k
 // grouping.  Not tuned for speed: it exists to measure accumulation error.
+#include "device.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void gemm_promotion_kernel(
     for (int64_t kb = 0; kb < KB; ++kb) {
       const a8i w = load_operand(brow + kb * 128, vn, g);
       const a8i x = load_operand(arow + kb * 128, vm, g);
-      chain = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, chain, 0, 0, 0, 127, 0, 127);
+      chain = mfma_e4m3_16x16x128(w, x, chain);
       if ((kb + 1) % per == 0 || kb + 1 == KB) {
         acc = acc + chain;
         chain = zero;
@@ -80,8 +81,7 @@ __global__ __launch_bounds__(256) void gemm_promotion_kernel(
       const a8i w = load_operand(brow + kb * 128, vn, g);
       const a8i x = load_operand(arow + kb * 128, vm, g);
       for (int lo = 0; lo < 128; lo += sub) {
-        const a4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            keep_range(w, g, lo, lo + sub), keep_range(x, g, lo, lo + sub), zero, 0, 0, 0, 127, 0, 127);
+        const a4f P = mfma_e4m3_16x16x128(keep_range(w, g, lo, lo + sub), keep_range(x, g, lo, lo + sub), zero);
         acc = acc + P;
       }
     }

@@ -1,6 +1,7 @@
 // C ABI of libfp8bs.so: host-side validation, device check, dispatch to the
 // kernel launchers.  Declarations and full contracts: include/fp8bs.h.
 #include "fp8bs.h"
+#include "fp8bs_probe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -259,15 +260,18 @@ fp8_status fp8_quant_act_tiles(const void* x, int64_t rows, int64_t cols, int64_
                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
-fp8_status fp8_probe_mfma(int64_t workgroups, int32_t iters, const uint8_t* codes, float* out,
-                          void* stream) {
+fp8_status fp8_probe_mfma(int64_t workgroups, int32_t iters, int32_t mode, const uint8_t* codes,
+                          float* out, void* stream) {
   if (workgroups < 1 || workgroups > (int64_t{1} << 20) || iters < 1) return FP8_ERR_SHAPE;
+  if (mode != FP8_PROBE_MFMA_PLAIN && mode != FP8_PROBE_MFMA_SCALED && mode != FP8_PROBE_MFMA_FOLD)
+    return FP8_ERR_SHAPE;
   if (!codes || !out) return FP8_ERR_NULL;
   if (!aligned16(codes) || !aligned4(out)) return FP8_ERR_ALIGN;
   if (overlap(span(codes, 1, 4096, 0), span(out, 1, workgroups * 256 * 4, 0))) return FP8_ERR_ALIAS;
   const fp8_status dev = check_device();
   if (dev != FP8_OK) return dev;
-  return launched(fp8bs::launch_mfma_probe(workgroups, iters, codes, out, reinterpret_cast<hipStream_t>(stream)));
+  return launched(fp8bs::launch_mfma_probe(workgroups, iters, mode, codes, out,
+                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
 fp8_status fp8_probe_recip_online(const float* s, float* r, int64_t n, void* stream) {

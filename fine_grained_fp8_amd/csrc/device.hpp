@@ -134,6 +134,16 @@ __device__ __forceinline__ uint32_t pack4_sat_nan(float a, float b, float c, flo
   return w;
 }
 
+// One 16x16x128 FP8 MFMA, E4M3 x E4M3 with FP32 accumulation and no block
+// scaling: D = A B + C.  The builtin names the block-scaled instruction;
+// with both scale operands (and their op_sel) zero the compiler selects the
+// plain v_mfma_f32_16x16x128_f8f6f4 instead, a single instruction where the
+// scaled form issues a scale-load prefix as well (twice the issue cycles
+// per MFMA).  The products are the same either way.
+__device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // 4x4 byte transpose: rows a0..a3 (byte j of a_i = element (i, j)) ->
 // columns o0..o3 (byte i of o_j = element (i, j)).
 __device__ __forceinline__ void transpose4x4_bytes(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,

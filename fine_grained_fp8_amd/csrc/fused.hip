@@ -16,7 +16,7 @@
 // an LDS stage, while the 128 weight rows of the block arrive in the same
 // stage by DMA.  Two stages: block kb+1 is loaded and quantized while block
 // kb is multiplied; one barrier per block.  The fold is the block GEMM's:
-// acc = fma(P, sx[m] * sw, acc) with P one v_mfma_scale_f32_16x16x128_f8f6f4.
+// acc = fma(P, sx[m] * sw, acc) with P one v_mfma_f32_16x16x128_f8f6f4.
 // Every output tile's workgroup quantizes its X rows again (N/128 times in
 // all); that repeated work is the price of fusion this kernel measures.
 // Workgroups of column tile 0 can also write the codes and scales out.
@@ -140,8 +140,13 @@ __global__ __launch_bounds__(256, 1) void fused_quant_fprop_kernel(FusedFpropPro
 
   load_block(0, lds[0]);
   quantize_block(0, lds[0]);
+  // the empty asm statements keep the compiler from moving LDS stores or
+  // loads across the wait and the barrier (both builtins are memory-neutral
+  // to it)
+  __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
   for (int kb = 0; kb < KB; ++kb) {
     uint8_t* cur = lds[kb & 1];
     uint8_t* nxt = lds[(kb + 1) & 1];
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(256, 1) void fused_quant_fprop_kernel(FusedFpropPro
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
-        const v4f P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wop[i], xop, zero, 0, 0, 0, 127, 0, 127);
+        const v4f P = mfma_e4m3_16x16x128(wop[i], xop, zero);
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(P[v], c, acc[i][j][v]);
       }
@@ -168,8 +173,10 @@ __global__ __launch_bounds__(256, 1) void fused_quant_fprop_kernel(FusedFpropPro
     if (more) quantize_block(kb + 1, nxt);
     // block kb+1's codes written and its weights landed; every wave done
     // with block kb's stage before block kb+2 is loaded into it
+    __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

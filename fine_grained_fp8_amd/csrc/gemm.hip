@@ -12,13 +12,14 @@
 // section 1 (forward, input-gradient and weight-gradient products).
 //
 // Design (CDNA4):
-//  * One v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, block scales 2^0)
-//    covers exactly one 128-wide K block of a 16x16 output tile, so each
-//    block's partial sum P comes out of a single MFMA with a zero accumulator
-//    and is folded into the running FP32 total with one FMA per element:
+//  * One v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3, no block scaling) covers
+//    exactly one 128-wide K block of a 16x16 output tile, so each block's
+//    partial sum P comes out of a single MFMA with a zero accumulator and is
+//    folded into the running FP32 total with one FMA per element:
 //    acc = fma(P, sa * sb, acc) - the promotion to FP32 at every 128-element
-//    interval that the method prescribes.  The MFMA's own E8M0 block scales
-//    stay at 2^0 because the method's FP32 scales are not powers of two.
+//    interval that the method prescribes.  The instruction's block-scaled
+//    form is not used: the method's FP32 scales are not powers of two, and
+//    its scale-load prefix would double the issue cost of every MFMA.
 //  * The weight-side operand is the MFMA "A" (rows = output columns n) and the
 //    token-side operand the MFMA "B" (columns = output rows m): each lane owns
 //    4 consecutive n of one output row m, and in Fprop/Dgrad one weight-block
@@ -133,11 +134,14 @@ __device__ __forceinline__ bool decode_tile(const GemmProblem& p, int64_t total_
   sBp = p.sB;
   if (grouped) {
     if (b >= total_tiles) return false;
+    // Offsets come from device memory unchecked: clamp each group into
+    // [0, M] with hi >= lo, so a malformed array can only empty or overlap
+    // groups, never move a row access outside A, sA or C.
     int64_t cum = 0, lo = 0, hi = 0, ntm = 0;
     int g = 0;
     for (; g < p.groups; ++g) {
-      lo = p.offsets[g];
-      hi = p.offsets[g + 1];
+      lo = min(max((int64_t)p.offsets[g], (int64_t)0), p.M);
+      hi = min(max((int64_t)p.offsets[g + 1], lo), p.M);
       ntm = (hi - lo + BM - 1) / BM;
       if (b < cum + ntm * tiles_n) break;
       cum += ntm * tiles_n;
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
-        Pc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bx[j], zero, 0, 0, 0, 127, 0, 127);
+        Pc[j] = mfma_e4m3_16x16x128(a[i], bx[j], zero);
         if (i > 0) fold(i - 1, j, Pp[j]);
       }
       if (i < kOpsPerBlock / 2) {
@@ -714,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
 #pragma unroll
       for (int i = 0; i < DNI; ++i) {
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
-        Pc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wc[i], bj, zero, 0, 0, 0, 127, 0, 127);
+        Pc[i] = mfma_e4m3_16x16x128(wc[i], bj, zero);
         __builtin_amdgcn_sched_barrier(0);
         if (j > 0) fold(acc[i][j - 1], Pp[i], c[j - 1], i);
         else if constexpr (kBlockW) fold(acc[i][DNJ - 1], Pl[i], cl, i);

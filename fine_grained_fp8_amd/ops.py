@@ -338,16 +338,24 @@ def gemm_promotion(A: torch.Tensor, B: torch.Tensor, promote_k: int, *, stream=N
     return C
 
 
-def probe_mfma(codes: torch.Tensor, workgroups: int, iters: int, *, stream=None):
+PROBE_MFMA_MODES = {"plain": 0, "scaled": 1, "fold": 2}
+
+
+def probe_mfma(codes: torch.Tensor, workgroups: int, iters: int, mode: str = "plain", *, stream=None):
     """Measurement aid: `workgroups` x 4 waves each run 8 * iters independent
     FP8 MFMAs (65,536 FLOP each) on operands taken from `codes` (4096 uint8
     E4M3 codes: A from bytes 32 l.., B from 2048 + 32 l.. for lane l), with no
-    memory traffic.  Returns the per-lane checksums [workgroups * 256] float32."""
+    memory traffic.  mode: "plain" (the GEMMs' MFMA), "scaled" (its
+    block-scaled encoding, scales 2^0) or "fold" (plain MFMAs each followed by
+    the 4 FP32 FMAs of the GEMMs' per-block fold).  Returns the per-lane
+    checksums [workgroups * 256] float32."""
     lib = _lib.load_library()
     if codes.dtype != torch.uint8 or codes.numel() < 4096 or not codes.is_contiguous():
         raise ValueError("codes: a contiguous uint8 tensor of at least 4096 elements")
+    if mode not in PROBE_MFMA_MODES:
+        raise ValueError(f"mode: one of {sorted(PROBE_MFMA_MODES)}")
     out = torch.empty(workgroups * 256, dtype=torch.float32, device=codes.device)
-    st = lib.fp8_probe_mfma(workgroups, iters, _ptr(codes), _ptr(out), _stream(stream))
+    st = lib.fp8_probe_mfma(workgroups, iters, PROBE_MFMA_MODES[mode], _ptr(codes), _ptr(out), _stream(stream))
     _lib.check("fp8_probe_mfma", st)
     return out
 

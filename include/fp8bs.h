@@ -260,9 +260,16 @@ fp8_status fp8_block_gemm_fused_quant(int64_t M, int64_t N, int64_t K, const voi
  *     for g in [0, groups): rows offsets[g] .. offsets[g+1]-1 of A and C use
  *     expert weights B_g.
  *  offsets_dev  DEVICE int32 [groups + 1], non-decreasing prefix sums with
- *               offsets[0] == 0 and offsets[groups] == total_M (the caller
- *               guarantees this; it is not read on the host).  Empty groups
- *               are allowed.
+ *               offsets[0] == 0 and offsets[groups] == total_M.  It is not
+ *               read on the host.  Empty groups are allowed.  The kernel
+ *               clamps what it reads so that no access leaves rows
+ *               [0, total_M) of A, sA and C whatever the array holds: group
+ *               g covers rows [lo, hi) with lo = min(max(offsets[g], 0),
+ *               total_M) and hi = min(max(offsets[g+1], lo), total_M), so a
+ *               decreasing pair gives an empty group.  For an array that
+ *               breaks the contract the values of C are unspecified (clamped
+ *               groups may overlap, and rows past the launch's tile budget
+ *               stay unwritten), but C is never written outside those rows.
  *  A   X_q [total_M][lda >= K];  sA [K/128][ld_sa >= total_M]
  *  B   W_q [groups][N][ldb >= K] (group g at B + g * N * ldb)
  *  sB  [groups][N/128][K/128] contiguous
@@ -393,38 +400,6 @@ fp8_status fp8_unpack_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t s
  */
 fp8_status fp8_dequant_tokens(const uint8_t* msg, int64_t T, int64_t H, int64_t stride, void* y,
                               int64_t ldy, void* stream);
-
-/*
- * fp8_probe_mfma - measurement aid for the GEMMs' roofline, not a step of the
- * method: each wave runs 8 independent accumulator chains of the GEMMs' FP8
- * MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, block scales 2^0) for `iters`
- * rounds with no memory traffic, so its duration gives the matrix-unit rate
- * the chip sustains on the given operand bytes (the clock under load depends
- * on the power the data draws).
- *  workgroups  1..2^20 workgroups of 256 threads (four waves); each wave does
- *              8 * iters MFMAs of 65,536 FLOP
- *  iters       >= 1
- *  codes       device, 4096 bytes of E4M3 codes: lane l of every wave takes
- *              operand A from bytes [32 l, 32 l + 32) and B from
- *              [2048 + 32 l, 2048 + 32 l + 32); 16-byte aligned
- *  out         device, workgroups * 256 floats: per lane, the sum of its
- *              accumulators (a checksum that keeps the work observable)
- *  Errors: FP8_ERR_SHAPE, FP8_ERR_NULL, FP8_ERR_ALIGN, FP8_ERR_ALIAS,
- *  FP8_ERR_DEVICE, FP8_ERR_LAUNCH.
- */
-fp8_status fp8_probe_mfma(int64_t workgroups, int32_t iters, const uint8_t* codes, float* out,
-                          void* stream);
-
-/*
- * fp8_probe_recip_online - verification aid: r[i] = the reciprocal the
- * quantizers use for an online scale s[i] (the hardware estimate refined by
- * one Newton step through FMAs), so a test can check it against the IEEE
- * reciprocal on every scale the online rule produces.
- *  s, r   device, n floats each, 4-byte aligned, not overlapping; 0 <= n <= 2^30
- *  Errors: FP8_ERR_SHAPE, FP8_ERR_NULL, FP8_ERR_ALIGN, FP8_ERR_ALIAS,
- *  FP8_ERR_DEVICE, FP8_ERR_LAUNCH.
- */
-fp8_status fp8_probe_recip_online(const float* s, float* r, int64_t n, void* stream);
 
 /* Static string naming a status; never NULL. */
 const char* fp8_status_string(fp8_status s);

@@ -11,7 +11,7 @@ import torch
 import synthetic as syn
 from oracle import gemm as og
 from oracle import quant
-from tolerance import check_gemm, truncation_bound
+from tolerance import check_gemm, truncation_bound, truncation_bound_at
 
 pytestmark = pytest.mark.gpu
 
@@ -71,3 +71,31 @@ def test_fused_quant_fprop_without_codes(gpu_lib):
     Cu = gpu_lib.block_gemm("fprop", qu, su, dev(Wq), dev(sW))
     torch.cuda.synchronize()
     assert torch.equal(C.view(torch.int16), Cu.view(torch.int16))
+
+
+def test_fused_quant_fprop_full_size(gpu_lib, big_layer):
+    """The bench's layer at full size (X 4096x7168 with outliers, W_q
+    18432x7168): the codes and scales the fused kernel forms equal the
+    oracle's, its output equals quantize-then-GEMM bit for bit, and one row
+    per M tile is checked against the oracle."""
+    Xq, sX, Wq, sW = big_layer
+    xb = syn.activation_with_outliers(4096, 7168, seed=0)
+    x = dev(xb)
+    del xb
+    W, S = dev(Wq), dev(sW)
+    C, q, s = gpu_lib.block_gemm_fused_quant(x, W, S, with_codes=True)
+    qu, su, _ = gpu_lib.quant_act_1x128(x, "row")
+    Cu = gpu_lib.block_gemm("fprop", qu, su, W, S)
+    torch.cuda.synchronize()
+    assert torch.equal(q, qu)
+    assert torch.equal(s[:, :4096].view(torch.int32), su[:, :4096].view(torch.int32))
+    assert torch.equal(C.view(torch.int16), Cu.view(torch.int16))
+    assert np.array_equal(q.cpu().numpy(), Xq)
+    assert np.array_equal(s[:, :4096].cpu().numpy().T.view(np.uint32), sX.view(np.uint32))
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([[0, 4095], np.arange(0, 4096, 128) + rng.integers(0, 128, 32)]))
+    R, T = og.fprop(Xq[rows], sX[rows], Wq, sW, with_magnitude=True)
+    sWn = og.expand_block_scales(sW, 18432)
+    check_gemm(C.view(torch.int16).cpu().numpy().view(np.uint16)[rows], R, T, 7168,
+               label="fused quant+fprop 4096x18432x7168",
+               E_at=lambda r, c: truncation_bound_at(Xq[rows], sX[rows], Wq, sWn, r, c))

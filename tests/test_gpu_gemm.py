@@ -12,7 +12,7 @@ import torch
 import synthetic as syn
 from oracle import gemm as og
 from oracle import quant
-from tolerance import check_gemm, truncation_bound
+from tolerance import check_gemm, truncation_bound, truncation_bound_at
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +35,25 @@ def act_scales_dev(s_rows):
 
 def bf16_bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def rows_one_per_tile(M, seed, tile=128):
+    """One seeded row in every 128-row tile of an M-row output, plus the first
+    and the last row: every M tile of the launch is sampled."""
+    rng = np.random.default_rng(seed)
+    starts = np.arange(0, M, tile)
+    picks = starts + rng.integers(0, np.minimum(tile, M - starts))
+    return np.unique(np.concatenate([[0, M - 1], picks]))
+
+
+def tiled_bytes(q):
+    """Operand-tiled bytes of row-major codes q [R][C] (R % 16 == 0,
+    C % 128 == 0), returned in a [R][C] array: oracle.tiling's layout written
+    as one reshape (pinned to tiling.tile_codes in
+    test_tiled_bytes_reshape_matches_the_oracle_layout)."""
+    R, C = q.shape
+    t = np.asarray(q, np.uint8).reshape(R // 16, 16, C // 128, 2, 4, 16).transpose(0, 2, 3, 4, 1, 5)
+    return np.ascontiguousarray(t).reshape(R, C)
 
 
 def run_fprop(fp8, Xq, sX, Wq, sW, out_dtype=torch.bfloat16):
@@ -100,27 +119,30 @@ def test_many_tiles_per_workgroup_ragged(gpu_lib, out_dtype):
     assert torch.equal(C.view(view), Ct.view(view))
 
 
-@pytest.fixture(scope="module")
-def big_layer():
-    """Oracle-quantized X (4096 x 7168, outliers) and W (18432 x 7168)."""
-    xb = syn.activation_with_outliers(4096, 7168, seed=0)
-    wb = syn.gaussian((18432, 7168), seed=1, std=0.02)
-    Xq, sX = quant.quant_rows(xb)
-    del xb
-    Wq, sW = quant.quant_weight(wb)
-    del wb
-    return Xq, sX, Wq, sW
-
-
 def test_fprop_full_size_sampled(gpu_lib, big_layer):
+    """The configuration the bench times (operand-tiled weight codes,
+    4096x18432x7168, persistent workgroups walking 9 tiles each, the next
+    tile's loads overlapping the current tile's stores): one output row in
+    every 128-row tile against the oracle, and a second launch byte-identical
+    to the first."""
     Xq, sX, Wq, sW = big_layer
-    C = run_fprop(gpu_lib, Xq, sX, Wq, sW)
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 6, replace=False)]))
+    A, sA, B, sB = dev(Xq), act_scales_dev(sX), dev(tiled_bytes(Wq)), dev(sW)
+    C = gpu_lib.block_gemm("fprop_tiled", A, sA, B, sB)
+    C2 = gpu_lib.block_gemm("fprop_tiled", A, sA, B, sB)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16)), "two launches differ"
+    rows = rows_one_per_tile(4096, seed=3)
     R, T = og.fprop(Xq[rows], sX[rows], Wq, sW, with_magnitude=True)
-    E = truncation_bound(Xq[rows], sX[rows], Wq, og.expand_block_scales(sW, 18432))
-    stats = check_gemm(bf16_bits(C)[rows], R, T, 7168, E=E, label="fprop 4096x18432x7168")
+    sWn = og.expand_block_scales(sW, 18432)
+    stats = check_gemm(bf16_bits(C)[rows], R, T, 7168, label="fprop_tiled 4096x18432x7168",
+                       E_at=lambda r, c: truncation_bound_at(Xq[rows], sX[rows], Wq, sWn, r, c))
     assert stats["n"] == rows.size * 18432
+
+
+def test_tiled_bytes_reshape_matches_the_oracle_layout():
+    from oracle import tiling
+    q = np.random.default_rng(9).integers(0, 256, (48, 384), dtype=np.uint8)
+    assert np.array_equal(tiled_bytes(q).ravel(), tiling.tile_codes(q))
 
 
 def test_fprop_deterministic(gpu_lib):
@@ -160,11 +182,12 @@ def test_dgrad_full_size_sampled(gpu_lib, big_layer):
     del dyb
     C = run_dgrad(gpu_lib, dYq, s_dY, Wq, sW)
     rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 4, replace=False)]))
+    rows = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 6, replace=False)]))
     R, T = og.dgrad(dYq[rows], s_dY[rows], Wq, sW, with_magnitude=True)
-    E = truncation_bound(dYq[rows], s_dY[rows], np.ascontiguousarray(Wq.T),
-                         og.expand_block_scales(np.ascontiguousarray(sW.T), 7168))
-    check_gemm(bf16_bits(C)[rows], R, T, 18432, E=E, label="dgrad 4096x7168x18432")
+    Wt = np.ascontiguousarray(Wq.T)
+    sWt = og.expand_block_scales(np.ascontiguousarray(sW.T), 7168)
+    check_gemm(bf16_bits(C)[rows], R, T, 18432, label="dgrad (LDS) 4096x7168x18432",
+               E_at=lambda r, c: truncation_bound_at(dYq[rows], s_dY[rows], Wt, sWt, r, c))
 
 
 def run_dgrad_t(fp8, dYq, s_dY, Wq_t, sW):
@@ -194,17 +217,23 @@ def test_dgrad_t_small_with_gpu_transposed_codes(gpu_lib):
 
 
 def test_dgrad_t_full_size_sampled(gpu_lib, big_layer):
+    """The bench's Dgrad (operand-tiled W_q^T, 4096x7168x18432): one row per
+    M tile against the oracle; two launches byte-identical."""
     _, _, Wq, sW = big_layer
     dyb = syn.gaussian((4096, 18432), seed=4, std=1e-3)
     dYq, s_dY = quant.quant_rows(dyb)
     del dyb
-    C = run_dgrad_t(gpu_lib, dYq, s_dY, np.ascontiguousarray(Wq.T), sW)
-    rng = np.random.default_rng(6)
-    rows = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 4, replace=False)]))
+    Wt = np.ascontiguousarray(Wq.T)
+    A, sA, B, sB = dev(dYq), act_scales_dev(s_dY), dev(tiled_bytes(Wt)), dev(sW)
+    C = gpu_lib.block_gemm("dgrad_t_tiled", A, sA, B, sB)
+    C2 = gpu_lib.block_gemm("dgrad_t_tiled", A, sA, B, sB)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16)), "two launches differ"
+    rows = rows_one_per_tile(4096, seed=6)
     R, T = og.dgrad(dYq[rows], s_dY[rows], Wq, sW, with_magnitude=True)
-    E = truncation_bound(dYq[rows], s_dY[rows], np.ascontiguousarray(Wq.T),
-                         og.expand_block_scales(np.ascontiguousarray(sW.T), 7168))
-    check_gemm(bf16_bits(C)[rows], R, T, 18432, E=E, label="dgrad_t 4096x7168x18432")
+    sWt = og.expand_block_scales(np.ascontiguousarray(sW.T), 7168)
+    check_gemm(bf16_bits(C)[rows], R, T, 18432, label="dgrad_t_tiled 4096x7168x18432",
+               E_at=lambda r, c: truncation_bound_at(dYq[rows], s_dY[rows], Wt, sWt, r, c))
 
 
 def run_wgrad(fp8, dYt, s_dy, Xt, s_x, out_dtype=torch.float32):
@@ -228,18 +257,24 @@ def test_wgrad_small(gpu_lib, out):
 
 
 def test_wgrad_full_size_sampled(gpu_lib):
+    """The bench's Wgrad (operand-tiled X_q^T, 18432x7168x4096, FP32 out):
+    one row per M tile (144) against the oracle; two launches
+    byte-identical."""
     dyb = syn.gaussian((4096, 18432), seed=4, std=1e-3)
     xb = syn.activation_with_outliers(4096, 7168, seed=0)
     dYt, s_dy = quant.quant_cols(dyb)
     del dyb
     Xt, s_x = quant.quant_cols(xb)
     del xb
-    C = run_wgrad(gpu_lib, dYt, s_dy, Xt, s_x)
-    rng = np.random.default_rng(6)
-    rows = np.unique(np.concatenate([[0, 18431], rng.choice(18432, 6, replace=False)]))
+    A, sA, B, sB = dev(dYt), act_scales_dev(s_dy), dev(tiled_bytes(Xt)), act_scales_dev(s_x)
+    C = gpu_lib.block_gemm("wgrad_tiled", A, sA, B, sB, out_dtype=torch.float32)
+    C2 = gpu_lib.block_gemm("wgrad_tiled", A, sA, B, sB, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int32), C2.view(torch.int32)), "two launches differ"
+    rows = rows_one_per_tile(18432, seed=6)
     R, T = og.wgrad(dYt[rows], s_dy[rows], Xt, s_x, with_magnitude=True)
-    E = truncation_bound(dYt[rows], s_dy[rows], Xt, s_x)
-    check_gemm(C.cpu().numpy()[rows], R, T, 4096, out="fp32", E=E, label="wgrad 18432x7168x4096")
+    check_gemm(C.cpu().numpy()[rows], R, T, 4096, out="fp32", label="wgrad_tiled 18432x7168x4096",
+               E_at=lambda r, c: truncation_bound_at(dYt[rows], s_dy[rows], Xt, s_x, r, c))
 
 
 def run_grouped(fp8, Xq, sX, offsets, Wq_e, sW_e):
@@ -264,6 +299,11 @@ def test_grouped_small_with_empty_and_tiny_groups(gpu_lib):
 
 
 def test_grouped_full_size_sampled(gpu_lib):
+    """Config 5 as the bench times it (8 experts, 16384 tokens split by a
+    seeded multinomial, N 2048, K 7168, operand-tiled expert weights): one row
+    per M tile of every expert (its first and last row included) against the
+    oracle, the tiled launch bit-identical to the row-major one, and two
+    tiled launches byte-identical."""
     counts = syn.expert_counts(16384, 8, seed=0)
     off = syn.expert_offsets(counts)
     xb = syn.activation_with_outliers(16384, 7168, seed=0)
@@ -271,15 +311,57 @@ def test_grouped_full_size_sampled(gpu_lib):
     del xb
     ws = [quant.quant_weight(syn.gaussian((2048, 7168), seed=100 + e, std=0.02)) for e in range(8)]
     Wq_e, sW_e = [w[0] for w in ws], [w[1] for w in ws]
-    C = run_grouped(gpu_lib, Xq, sX, off, Wq_e, sW_e)
+    offd, A, sA = dev(off.astype(np.int32)), dev(Xq), act_scales_dev(sX)
+    S = dev(np.stack(sW_e))
+    C_rm = gpu_lib.block_gemm_grouped(offd, A, sA, dev(np.stack(Wq_e)), S)
+    Bt = dev(np.stack([tiled_bytes(w) for w in Wq_e]))
+    C = gpu_lib.block_gemm_grouped(offd, A, sA, Bt, S, tiled=True)
+    C2 = gpu_lib.block_gemm_grouped(offd, A, sA, Bt, S, tiled=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C_rm.view(torch.int16)), "tiled and row-major differ"
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16)), "two launches differ"
     y = bf16_bits(C)
-    rng = np.random.default_rng(7)
     for e in range(8):
         lo, hi = int(off[e]), int(off[e + 1])
-        rows = np.unique(np.concatenate([[lo, hi - 1], lo + rng.choice(hi - lo, 2, replace=False)]))
+        rows = lo + rows_one_per_tile(hi - lo, seed=7 + e)
         R, T = og.fprop(Xq[rows], sX[rows], Wq_e[e], sW_e[e], with_magnitude=True)
-        E = truncation_bound(Xq[rows], sX[rows], Wq_e[e], og.expand_block_scales(sW_e[e], 2048))
-        check_gemm(y[rows], R, T, 7168, E=E, label=f"grouped expert {e}")
+        sWn = og.expand_block_scales(sW_e[e], 2048)
+        check_gemm(y[rows], R, T, 7168, label=f"grouped_tiled expert {e} ({hi - lo} rows)",
+                   E_at=lambda r, c: truncation_bound_at(Xq[rows], sX[rows], Wq_e[e], sWn, r, c))
+
+
+def test_grouped_malformed_offsets_stay_inside_the_rows(gpu_lib):
+    """Offsets that break the contract (past total_M, decreasing, negative)
+    are clamped on the device: C has guard rows beyond total_M that must keep
+    their sentinel, the well-formed leading groups are still exact, and
+    nothing faults.  Every access stays inside the allocations by
+    construction: A, sA and C hold total_M (+ guard) rows."""
+    total_M, N, K = 300, 256, 256
+    xb = syn.activation_with_outliers(total_M, K, seed=121)
+    Xq, sX = quant.quant_rows(xb)
+    ws = [quant.quant_weight(syn.gaussian((N, K), seed=122 + e, std=0.02)) for e in range(5)]
+    Wq_e, sW_e = [w[0] for w in ws], [w[1] for w in ws]
+    B, S = dev(np.stack(Wq_e)), dev(np.stack(sW_e))
+    guard = 64
+    sentinel = 0x5A5A
+    # (offsets, whether rows 0..99 stay group 0's alone after the clamp)
+    for off, exact0 in (([0, 100, 5000, 150, 120, 300], True),
+                        ([0, 100, 250, 2**31 - 1, 2**31 - 1, 2**31 - 1], True),
+                        ([-50, 100, 200, 150, -7, 400], False)):
+        offd = dev(np.asarray(off, np.int32))
+        for tiled in (False, True):
+            Cbuf = torch.full((total_M + guard, N), sentinel, dtype=torch.int16, device="cuda")
+            Bx = dev(np.stack([tiled_bytes(w) for w in Wq_e])) if tiled else B
+            gpu_lib.block_gemm_grouped(offd, dev(Xq), act_scales_dev(sX), Bx, S, tiled=tiled,
+                                       out=Cbuf[:total_M].view(torch.bfloat16))
+            torch.cuda.synchronize()
+            assert torch.all(Cbuf[total_M:] == sentinel).item(), (off, tiled)
+            if not exact0:
+                continue
+            R, T = og.fprop(Xq[:100], sX[:100], Wq_e[0], sW_e[0], with_magnitude=True)
+            check_gemm(Cbuf[:100].cpu().numpy().view(np.uint16), R, T, K,
+                       E=truncation_bound(Xq[:100], sX[:100], Wq_e[0], og.expand_block_scales(sW_e[0], N)),
+                       label=f"grouped clamp {off[:4]} tiled={tiled}")
 
 
 # ---------------------------------------------------------------------------
@@ -392,13 +474,18 @@ def test_tiled_wgrad_full_size_bit_identical(gpu_lib):
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
-def test_probe_mfma_counts_its_work(gpu_lib):
-    """The rate probe runs 8 * iters MFMAs per wave: with every code 1.0 each
-    of a lane's 4 outputs per chain gains 128 per MFMA, so its checksum is
-    8 * 4 * 128 * iters; with zero codes it is 0."""
+@pytest.mark.parametrize("mode", ["plain", "scaled", "fold"])
+def test_probe_mfma_counts_its_work(gpu_lib, mode):
+    """The rate probe runs 8 * iters MFMAs per wave in every mode: with every
+    code 1.0 each of a lane's 4 outputs per chain gains 128 per MFMA (the
+    fold multiplies by 1.0), so its checksum is 8 * 4 * 128 * iters; with
+    zero codes it is 0.  Odd and even iteration counts (the fold mode runs
+    rounds in pairs)."""
     ones = torch.full((4096,), 0x38, dtype=torch.uint8, device="cuda")
-    out = gpu_lib.probe_mfma(ones, 3, 5)
-    zero = gpu_lib.probe_mfma(torch.zeros(4096, dtype=torch.uint8, device="cuda"), 2, 7)
+    out = gpu_lib.probe_mfma(ones, 3, 5, mode)
+    out6 = gpu_lib.probe_mfma(ones, 2, 6, mode)
+    zero = gpu_lib.probe_mfma(torch.zeros(4096, dtype=torch.uint8, device="cuda"), 2, 7, mode)
     torch.cuda.synchronize()
     assert torch.all(out == 8 * 4 * 128 * 5).item()
+    assert torch.all(out6 == 8 * 4 * 128 * 6).item()
     assert torch.all(zero == 0).item()

@@ -8,23 +8,30 @@ import os
 import re
 import shutil
 import subprocess
+import sys
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
 def lib():
     from fine_grained_fp8_amd import _lib, build
+    sanitized = os.environ.get("FP8BS_SANITIZED_LIB")
+    if sanitized:
+        # the host-only sanitizer build of the same validation code (see
+        # test_validation_layer_under_asan_ubsan)
+        return _lib.load_library(sanitized)
     if not os.path.exists(_lib.LIB_PATH):
         build.build()
     return _lib.load_library()
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fp8_[a-z0-9_]+)\s*\(", text)))
 
@@ -272,9 +279,11 @@ def test_probe_recip_validation(lib):
 
 
 def test_probe_mfma_validation(lib):
-    f = lambda wg=4, it=2, codes=A, out=C: lib.fp8_probe_mfma(wg, it, codes, out, None)
+    f = lambda wg=4, it=2, mode=0, codes=A, out=C: lib.fp8_probe_mfma(wg, it, mode, codes, out, None)
     assert f(wg=0) == SHAPE
     assert f(it=0) == SHAPE
+    assert f(mode=3) == SHAPE
+    assert f(mode=-1) == SHAPE
     assert f(codes=None) == NULL
     assert f(out=None) == NULL
     assert f(codes=A + 8) == ALIGN
@@ -372,3 +381,40 @@ def test_division_shortcut_exhaustive(tmp_path):
     assert "mismatches=0" in res.stdout
     assert "pairs=1065402240" in res.stdout
     assert "scales=32640 scale_mismatches=0" in res.stdout
+
+
+def test_validation_layer_under_asan_ubsan(tmp_path):
+    """The C-ABI layer (api.cpp: argument checks, range and alias
+    arithmetic, device query) built on the host with g++
+    -fsanitize=address,undefined, the kernel launchers replaced by host stubs
+    (tests/c/launch_stubs.cpp), runs every validation test of this file in a
+    child process without a sanitizer report.  No device code is built or
+    run here."""
+    if os.environ.get("FP8BS_SANITIZED_LIB"):
+        pytest.skip("already the sanitized child run")
+    gxx = shutil.which("g++")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    if not gxx or not os.path.exists(os.path.join(rocm, "include", "hip", "hip_runtime.h")):
+        pytest.skip("g++ or the HIP headers are not available")
+    lib_path = str(tmp_path / "libfp8bs_san.so")
+    csrc = os.path.join(ROOT, "fine_grained_fp8_amd", "csrc")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"), "-I", csrc,
+           os.path.join(csrc, "api.cpp"), os.path.join(ROOT, "tests", "c", "launch_stubs.cpp"),
+           "-L", os.path.join(rocm, "lib"), "-Wl,-rpath," + os.path.join(rocm, "lib"), "-lamdhip64",
+           "-o", lib_path]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    asan = subprocess.run([gxx, "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    env = dict(os.environ, LD_PRELOAD=asan, FP8BS_SANITIZED_LIB=lib_path,
+               ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    sel = "(validation or status_strings or no_device) and not asan"
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.abspath(__file__), "-q", "-x",
+                        "-p", "no:cacheprovider", "-k", sel], env=env, capture_output=True, text=True,
+                       timeout=600, cwd=ROOT)
+    report = r.stdout[-3000:] + r.stderr[-3000:]
+    assert r.returncode == 0, report
+    assert "AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr, report
+    assert " passed" in r.stdout, report

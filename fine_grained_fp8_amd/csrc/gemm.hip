@@ -495,13 +495,11 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
 // together inside the MFMA.
 // ---------------------------------------------------------------------------
 constexpr int DNI = 4, DNJ = 8;                // wave tile: 64 (n) x 128 (m)
-constexpr int kDScaleOff = BM * BK;            // token-side scales (1 KB DMA footprint)
-constexpr int kDWScaleOff = kDScaleOff + 1024; // weight-side scales (1 KB)
+constexpr int kDScaleOff = BM * BK;            // token-side scales, [lrow][j] order (512 B)
+constexpr int kDWScaleOff = kDScaleOff + 1024; // Wgrad: the tile's per-column weight-side scales (1 KB)
 constexpr int kDStage = kDWScaleOff + 1024;    // 18 KB per stage
 constexpr int kDOutStage = 16384;              // epilogue staging per wave: 128 x 64 BF16 or 64 x 64 FP32
-constexpr int kDDmaOps = 4 + 1 + 1;            // DMA per block: 4 token-row, 2 scale instructions
 constexpr int kDWOps = 8;                      // weight loads per block
-constexpr int kDOpsPerBlock = kDDmaOps + kDWOps;
 
 template <int kLayout, bool kOutF32, bool kGrouped, bool kTiledB>
 __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProblem p, int64_t total_tiles,
@@ -524,6 +522,10 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   // next tile before it stores the current one.
   const int KB = (int)(p.K / BK);
   constexpr bool kBlockW = kLayout == kFprop || kLayout == kDgradT;
+  // DMA per block: 4 token-row instructions, the token-side scales and the
+  // weight-side scales; then the 8 weight loads
+  constexpr int kDDmaOps = 6;
+  constexpr int kDOpsPerBlock = kDDmaOps + kDWOps;
   int64_t m0 = 0, m_end = 0, n0 = 0;
   const uint8_t* Bp = p.B;
   const float* sBp = p.sB;
@@ -537,6 +539,10 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   // chunks XOR-swizzled by row & 7 (row & 7 == (lane >> 3) & 7 here)
   const int xrow = wave * 32 + (lane >> 3);
   const uint32_t off_x = (uint32_t)(xrow * (int)p.lda + (((lane & 7) ^ (lane >> 3)) << 4));
+  // token-scale DMA: lane l of wave w fetches the scale of row 16 j + lrow
+  // for LDS float t = 64 (w & 1) + l = 8 lrow + j
+  const int sc_t = 64 * (wave & 1) + lane;
+  const uint32_t sc_row_off = (uint32_t)(((sc_t & 7) * 16 + (sc_t >> 3)) * 4);
   // weight-side rows n0 + 64 wave + 16 i + lrow, loaded straight into
   // registers; row-major: lane reads 16 B of its row; operand-tiled (ldb ==
   // K): the wave's 16-row groups are 2 KB tiles per K block, each half one
@@ -586,24 +592,31 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_x, (lds_ptr_t)(st + (wave * 4 + op) * 1024), 16,
                                                off_x + (uint32_t)(kb * BK), (uint32_t)(op * 8 * (int)p.lda), 0, 0);
     } else if (op == 4) {
-      // 32-bit block offset (validated: the scale tables stay below 2^31
-      // bytes) on a per-tile base keeps the resource cheap to rebuild
+      // The token-side scales of this block, rows m0..m0+127, land in LDS in
+      // [lrow][j] order (float 8 lrow + j holds row 16 j + lrow) so a lane
+      // reads its 8 scales as two 16-byte runs.  One float per lane: waves
+      // 0 and 2 write floats 0..63, waves 1 and 3 floats 64..127 (identical
+      // bytes).  32-bit block offset (validated: the scale tables stay below
+      // 2^31 bytes) on a per-tile base keeps the resource cheap to rebuild.
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(reinterpret_cast<const uint8_t*>(sa_tile) + (uint32_t)kb * sa_kbytes), (short)0, rows_m * 4,
           (int)kRsrcWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + kDScaleOff), 16, (uint32_t)(lane * 16), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + kDScaleOff + 256 * (wave & 1)), 4,
+                                               sc_row_off, 0, 0, 0);
     } else if (op == 5) {
       if constexpr (kLayout == kWgrad) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(reinterpret_cast<const uint8_t*>(sb_tile) + (uint32_t)kb * sb_kbytes), (short)0, rows_n * 4,
             (int)kRsrcWord3);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + kDWScaleOff), 16, (uint32_t)(lane * 16), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + kDWScaleOff), 16, (uint32_t)(lane * 16), 0, 0,
+                                                 0);
       } else {
+        // the wave's weight-block scale (every lane fetches the same float)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_sw, (lds_ptr_t)(st + kDWScaleOff + wave * 256), 4,
                                                  sw_off + (uint32_t)kb * sw_kstride, 0, 0, 0);
       }
     } else {
-      const int i = (op - 6) >> 1, h = (op - 6) & 1;
+      const int i = (op - kDDmaOps) >> 1, h = (op - kDDmaOps) & 1;
       const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
           rsrc_w, off_w + (uint32_t)kb * w_kstride, (uint32_t)i * w_istride + (uint32_t)h * w_hstride, 0);
       wr[i][4 * h + 0] = v[0];
@@ -653,12 +666,17 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     cl = 0.f;
   };
 
+  auto read_tn = [&](const uint8_t* stn, int half) {
+    const float4 t = *reinterpret_cast<const float4*>(stn + kDScaleOff + lrow * 32 + half * 16);
+    tn[4 * half + 0] = t.x;
+    tn[4 * half + 1] = t.y;
+    tn[4 * half + 2] = t.z;
+    tn[4 * half + 3] = t.w;
+  };
   auto prefetch = [&](const uint8_t* stn) {
-    const float* sxl = reinterpret_cast<const float*>(stn + kDScaleOff);
-    const float* swl = reinterpret_cast<const float*>(stn + kDWScaleOff);
-    if constexpr (kBlockW) wn = swl[wave * 64];
-#pragma unroll
-    for (int j = 0; j < DNJ; ++j) tn[j] = sxl[j * 16 + lrow];
+    if constexpr (kBlockW) wn = reinterpret_cast<const float*>(stn + kDWScaleOff)[wave * 64];
+    read_tn(stn, 0);
+    read_tn(stn, 1);
     bxa = pair(stn + x_lo, stn + x_hi);
     bxb = pair(stn + x_lo + 2048, stn + x_hi + 2048);
   };
@@ -695,8 +713,6 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     v4i bxl[DNJ], bxh[DNJ];           // token-side operand halves, read two rows ahead
     bxl[0] = lo_half(bxa); bxh[0] = hi_half(bxa);
     bxl[1] = lo_half(bxb); bxh[1] = hi_half(bxb);
-    const float* sxn = reinterpret_cast<const float*>(stn + kDScaleOff);
-    const float* swn = reinterpret_cast<const float*>(stn + kDWScaleOff);
     v4i an_l, an_h, bn_l, bn_h;       // block kb+1's first two operand rows
     // rows j of 4 MFMAs (the wave's 4 weight subtiles against token subtile
     // j), each MFMA followed by the fold of the same subtile's partial from
@@ -730,7 +746,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
           if (i == 0) bxl[j + 2] = *reinterpret_cast<const v4i*>(st + x_lo + (j + 2) * 2048);
           if (i == 2) bxh[j + 2] = *reinterpret_cast<const v4i*>(st + x_hi + (j + 2) * 2048);
         }
-        if (j < kDOpsPerBlock / 2 && (i & 1)) {
+        if ((i & 1) && 2 * j + (i >> 1) < kDOpsPerBlock) {
           const int op = 2 * j + (i >> 1);
           issue_load(op < kDDmaOps ? kb_d : kb_w, op, sd, wf);
         }
@@ -743,13 +759,11 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
         if (j == DNJ - 1) {
           // the next block's scales; tn[0..7] are consumed by this step's
           // rows before these reads (c[j] above), so they can be refilled
-          if (i == 0) { tn[0] = sxn[lrow]; tn[1] = sxn[16 + lrow]; }
-          if (i == 1) { tn[2] = sxn[32 + lrow]; tn[3] = sxn[48 + lrow]; }
-          if (i == 2) {
-            tn[4] = sxn[64 + lrow]; tn[5] = sxn[80 + lrow];
-            if constexpr (kBlockW) wn = swn[wave * 64];
+          if (i == 0) read_tn(stn, 0);
+          if (i == 1) read_tn(stn, 1);
+          if constexpr (kBlockW) {
+            if (i == 2) wn = reinterpret_cast<const float*>(stn + kDWScaleOff)[wave * 64];
           }
-          if (i == 3) { tn[6] = sxn[96 + lrow]; tn[7] = sxn[112 + lrow]; }
         }
         // instruction order = source order: one MFMA, then the fold of the
         // partial it produced four MFMAs (20 instructions) earlier

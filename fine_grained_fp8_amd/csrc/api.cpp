@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -52,6 +53,74 @@ Range span(const void* p, int64_t rows, int64_t row_bytes, int64_t ld_bytes) {
   return {b, b + static_cast<uintptr_t>((rows - 1) * ld_bytes + row_bytes)};
 }
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// ---- split-K workspace of the persistent GEMM kernel ----
+// One per (device, stream), allocated on the first GEMM call on that stream
+// and kept until the process ends: partial tiles for one piece per
+// workgroup of a full-device launch, and the per-tile counters (zeroed once
+// on the stream; each launch leaves them zero).  Calls on one stream are
+// ordered, so they share it safely; calls on different streams get
+// different workspaces.  No workspace (and no split: the same results up to
+// FP32 summation order, the whole-tile schedule) when the stream is being
+// captured into a graph and has none yet, when the allocation fails, or when
+// kMaxWorkspaces are held.
+constexpr int kMaxWorkspaces = 64;
+struct Workspace {
+  int dev;
+  hipStream_t stream;
+  void* mem;
+  int64_t slots;
+};
+std::mutex g_ws_mutex;
+Workspace g_ws[kMaxWorkspaces];
+int g_ws_used = 0;
+
+// the workspace held for `stream` on the current device, or nullptr
+const Workspace* find_workspace(int dev, hipStream_t stream) {
+  for (int i = 0; i < g_ws_used; ++i)
+    if (g_ws[i].dev == dev && g_ws[i].stream == stream) return &g_ws[i];
+  return nullptr;
+}
+
+void attach_workspace(GemmProblem& p, hipStream_t stream) {
+  p.ws_partial = nullptr;
+  p.ws_count = nullptr;
+  p.ws_slots = 0;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  const Workspace* w = find_workspace(dev, stream);
+  if (w == nullptr) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
+    }
+    const int64_t slots = fp8bs::device_cus();
+    if (cap != hipStreamCaptureStatusNone || g_ws_used == kMaxWorkspaces || slots < 8) return;
+    void* mem = nullptr;
+    const size_t bytes = fp8bs::split_workspace_bytes(slots);
+    if (hipMalloc(&mem, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
+    }
+    const size_t count_off = (size_t)slots * (size_t)fp8bs::kSplitTileFloats * 4u;
+    if (hipMemsetAsync(static_cast<uint8_t*>(mem) + count_off, 0, (size_t)slots * 4u, stream) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFree(mem);
+      return;
+    }
+    g_ws[g_ws_used] = Workspace{dev, stream, mem, slots};
+    w = &g_ws[g_ws_used++];
+  }
+  p.ws_partial = static_cast<float*>(w->mem);
+  p.ws_count = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(w->mem) +
+                                           (size_t)w->slots * (size_t)fp8bs::kSplitTileFloats * 4u);
+  p.ws_slots = w->slots;
+}
 
 fp8_status launched(hipError_t e) {
   if (e != hipSuccess) {
@@ -274,6 +343,30 @@ fp8_status fp8_probe_mfma(int64_t workgroups, int32_t iters, int32_t mode, const
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
+fp8_status fp8_probe_gemm_split(int64_t tiles, int64_t K, void* stream, int64_t* split_tiles, int32_t* pieces) {
+  if (tiles < 0 || K <= 0 || K % 128 != 0) return FP8_ERR_SHAPE;
+  if (!split_tiles || !pieces) return FP8_ERR_NULL;
+  const fp8_status dev = check_device();
+  if (dev != FP8_OK) return dev;
+  int d = -1;
+  if (hipGetDevice(&d) != hipSuccess) {
+    (void)hipGetLastError();
+    return FP8_ERR_DEVICE;
+  }
+  int64_t slots = 0;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    const Workspace* w = find_workspace(d, reinterpret_cast<hipStream_t>(stream));
+    if (w) slots = w->slots;
+  }
+  const int64_t kb = K / 128;
+  const fp8bs::SplitPlan plan =
+      fp8bs::split_plan(tiles, fp8bs::persistent_grid(tiles), kb > (1 << 30) ? (1 << 30) : (int)kb, slots);
+  *split_tiles = plan.split_tiles;
+  *pieces = plan.split;
+  return FP8_OK;
+}
+
 fp8_status fp8_probe_recip_online(const float* s, float* r, int64_t n, void* stream) {
   if (n < 0 || n > (int64_t{1} << 30)) return FP8_ERR_SHAPE;
   if (n == 0) return FP8_OK;
@@ -412,6 +505,7 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
   p.C = C; p.ldc = ldc; p.out_fp32 = c_dtype == FP8_OUT_FP32;
   p.b_tiled = tiled ? 1 : 0;
   p.groups = 0; p.offsets = nullptr;
+  attach_workspace(p, reinterpret_cast<hipStream_t>(stream));
   return launched(fp8bs::launch_gemm(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -487,6 +581,7 @@ fp8_status grouped_impl(int32_t groups, const int32_t* offsets_dev, int64_t tota
   p.C = C; p.ldc = ldc; p.out_fp32 = c_dtype == FP8_OUT_FP32;
   p.b_tiled = tiled ? 1 : 0;
   p.groups = groups; p.offsets = offsets_dev;
+  attach_workspace(p, reinterpret_cast<hipStream_t>(stream));
   return launched(fp8bs::launch_gemm(p, reinterpret_cast<hipStream_t>(stream)));
 }
 }  // namespace

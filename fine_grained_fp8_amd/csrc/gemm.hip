@@ -120,20 +120,18 @@ __device__ __forceinline__ v8i read_operand_t(const uint8_t* tile, int n_sub, in
   return out;
 }
 
-// Tile `id` of a launch of `ids` tile ids: token rows [m0, min(m0 + BM,
+// Output tile `b` (0 <= b < the tile count): token rows [m0, min(m0 + BM,
 // m_end)) and output columns [n0, n0 + BN); Bp / sBp point at the tile's
-// group in the grouped case.  Returns false for the padding ids of a grouped
-// launch.
-__device__ __forceinline__ bool decode_tile(const GemmProblem& p, int64_t total_tiles, bool grouped,
-                                            int64_t id, int64_t ids,
-                                            int64_t& m0, int64_t& m_end, int64_t& n0,
-                                            const uint8_t*& Bp, const float*& sBp) {
+// group in the grouped case.  Tiles are numbered group by group (grouped) or
+// in the GroupM-swizzled order.  Returns false when b lies past the last
+// group.
+__device__ __forceinline__ bool decode_tile_index(const GemmProblem& p, bool grouped, int64_t b,
+                                                  int64_t& m0, int64_t& m_end, int64_t& n0,
+                                                  const uint8_t*& Bp, const float*& sBp) {
   const int64_t tiles_n = (p.N + BN - 1) / BN;
-  const int64_t b = xcd_remap(id, ids);
   Bp = p.B;
   sBp = p.sB;
   if (grouped) {
-    if (b >= total_tiles) return false;
     // Offsets come from device memory unchecked: clamp each group into
     // [0, M] with hi >= lo, so a malformed array can only empty or overlap
     // groups, never move a row access outside A, sA or C.
@@ -162,6 +160,30 @@ __device__ __forceinline__ bool decode_tile(const GemmProblem& p, int64_t total_
     m_end = p.M;
   }
   return true;
+}
+
+// Number of output tiles of a grouped launch, from the offsets as clamped by
+// decode_tile_index.
+__device__ __forceinline__ int64_t grouped_tile_count(const GemmProblem& p) {
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  int64_t cum = 0;
+  for (int g = 0; g < p.groups; ++g) {
+    const int64_t lo = min(max((int64_t)p.offsets[g], (int64_t)0), p.M);
+    const int64_t hi = min(max((int64_t)p.offsets[g + 1], lo), p.M);
+    cum += (hi - lo + BM - 1) / BM * tiles_n;
+  }
+  return cum;
+}
+
+// Tile of workgroup id `id` in a one-tile-per-workgroup launch of `ids`
+// workgroups; false for the padding ids of a grouped launch.
+__device__ __forceinline__ bool decode_tile(const GemmProblem& p, int64_t total_tiles, bool grouped,
+                                            int64_t id, int64_t ids,
+                                            int64_t& m0, int64_t& m_end, int64_t& n0,
+                                            const uint8_t*& Bp, const float*& sBp) {
+  const int64_t b = xcd_remap(id, ids);
+  if (grouped && b >= total_tiles) return false;
+  return decode_tile_index(p, grouped, b, m0, m_end, n0, Bp, sBp);
 }
 
 // Round and store 4 consecutive outputs (n..n+3) of row m; columns past N
@@ -495,32 +517,77 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_kernel(GemmProblem p, 
 // together inside the MFMA.
 // ---------------------------------------------------------------------------
 constexpr int DNI = 4, DNJ = 8;                // wave tile: 64 (n) x 128 (m)
-constexpr int kDScaleOff = BM * BK;            // token-side scales, [lrow][j] order (512 B)
-constexpr int kDWScaleOff = kDScaleOff + 1024; // Wgrad: the tile's per-column weight-side scales (1 KB)
-constexpr int kDStage = kDWScaleOff + 1024;    // 18 KB per stage
+constexpr int kDStage = BM * BK;               // token tile per stage: 16 KB
+// per-stage scales, an LDS object of their own so that the four tile stages
+// fill the first 64 KB and every operand read takes an immediate offset from
+// one base address
+constexpr int kDScaleOff = 0;                  // token-side scales, [lrow][j] order (512 B)
+constexpr int kDFreeOff = 512;                 // 512 B no DMA writes
+constexpr int kDWScaleOff = 1024;              // weight-side scales (Wgrad: 256 per-column floats)
+constexpr int kDScaleStage = 2048;
 constexpr int kDOutStage = 16384;              // epilogue staging per wave: 128 x 64 BF16 or 64 x 64 FP32
 constexpr int kDWOps = 8;                      // weight loads per block
 
 template <int kLayout, bool kOutF32, bool kGrouped, bool kTiledB>
-__global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProblem p, int64_t total_tiles,
-                                                                        int64_t tile_ids) {
+__global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProblem p, int64_t total_tiles) {
   static_assert(kLayout != kDgrad, "Dgrad reads the weights transposed through LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_s0[kDStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_s1[kDStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_s2[kDStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_s3[kDStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_out[4][kDOutStage];   // per-wave epilogue staging
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[kDStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[kDStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a2[kDStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a3[kDStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_c0[kDScaleStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_c1[kDScaleStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_c2[kDScaleStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_c3[kDScaleStage];
+  // per-wave epilogue staging, four objects of the stage size (one 64 KB
+  // array would be placed first and push the tile stages past the 64 KB
+  // reach of LDS instruction offsets)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_z0[kDOutStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_z1[kDOutStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_z2[kDOutStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_z3[kDOutStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 15, lgrp = lane >> 4;
+  // stage k: token tile in lds_ak, its scales in lds_ck (k a compile-time tag)
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  auto tile_of = [&](auto k) -> uint8_t* {
+    constexpr int s_ = decltype(k)::value;
+    if constexpr (s_ == 0) return lds_a0;
+    else if constexpr (s_ == 1) return lds_a1;
+    else if constexpr (s_ == 2) return lds_a2;
+    else return lds_a3;
+  };
+  auto scl_of = [&](auto k) -> uint8_t* {
+    constexpr int s_ = decltype(k)::value;
+    if constexpr (s_ == 0) return lds_c0;
+    else if constexpr (s_ == 1) return lds_c1;
+    else if constexpr (s_ == 2) return lds_c2;
+    else return lds_c3;
+  };
+  // the same stages as LDS-address-space pointers, for the DMA destinations
+  // (a cast of a generic pointer would carry a null check into M0)
+  using lds_u8 = __attribute__((address_space(3))) uint8_t;
+  auto tile_lds = [&](auto k) -> lds_u8* { return (lds_u8*)tile_of(k); };
+  auto scl_lds = [&](auto k) -> lds_u8* { return (lds_u8*)scl_of(k); };
 
-  // Persistent: the workgroup takes tile ids blockIdx.x, + gridDim.x, ... of
-  // the launch's `tile_ids` (gridDim.x is a multiple of 8, so all ids of a
-  // workgroup map to the same XCD's run of tiles), and starts the loads of its
-  // next tile before it stores the current one.
+  // Persistent: the workgroup takes work ids blockIdx.x, + gridDim.x, ...
+  // and starts the loads of its next tile before it stores the current one.
+  // Ids below plan.dp_tiles are whole tiles (gridDim.x is a multiple of 8,
+  // so all of a workgroup's tiles lie in the same XCD's run); the ids after
+  // them are the K pieces of the leftover tiles, one per workgroup, summed by
+  // the piece that finishes last.
   const int KB = (int)(p.K / BK);
+  const int64_t n_tiles = kGrouped ? uniform_i64(grouped_tile_count(p)) : total_tiles;
+  const SplitPlan plan = split_plan(n_tiles, gridDim.x, KB, p.ws_partial != nullptr ? p.ws_slots : 0);
+  const int64_t work_ids = plan.dp_tiles + plan.split_tiles * plan.split;
+  int kb_lo = 0, kb_hi = KB;        // the tile's K blocks
+  int piece_slot = -1;              // split piece: its workspace slot; -1: a whole tile
   constexpr bool kBlockW = kLayout == kFprop || kLayout == kDgradT;
   // DMA per block: 4 token-row instructions, the token-side scales and the
   // weight-side scales; then the 8 weight loads
@@ -559,9 +626,31 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   const int64_t sw_elems = kLayout == kFprop ? (p.N / 128) * p.ld_sb
                                              : (kLayout == kDgradT ? (p.K / BK) * p.ld_sb : 0);
   const uint32_t sw_kstride = kLayout == kFprop ? 4u : (uint32_t)p.ld_sb * 4u;
-  // decode tile id `id` and set up its buffer resources; false for padding ids
+  // decode work id `id` and set up its buffer resources; false if it names
+  // no tile
   auto setup_tile = [&](int64_t id) -> bool {
-    if (!decode_tile(p, total_tiles, kGrouped, id, tile_ids, m0, m_end, n0, Bp, sBp)) return false;
+    int64_t b;
+    if (id < plan.dp_tiles) {
+      b = xcd_remap(id, plan.dp_tiles);
+      kb_lo = 0;
+      kb_hi = KB;
+      piece_slot = -1;
+    } else {
+      // pieces in K-range-major order, each XCD a contiguous run of them: an
+      // XCD's pieces share one K range and neighbouring tiles, so its L2
+      // serves the token rows and weight columns they have in common
+      const int64_t pieces = plan.split_tiles * plan.split;
+      const int q = (int)xcd_remap(id - plan.dp_tiles, pieces);
+      const int range = q / (int)plan.split_tiles, t = q % (int)plan.split_tiles;
+      b = plan.dp_tiles + t;
+      int lo, hi;
+      split_range(plan, range, KB, lo, hi);
+      kb_lo = __builtin_amdgcn_readfirstlane(lo);
+      kb_hi = __builtin_amdgcn_readfirstlane(hi);
+      // the tile's partials lie together, in piece order
+      piece_slot = __builtin_amdgcn_readfirstlane(t * plan.split + range);
+    }
+    if (!decode_tile_index(p, kGrouped, b, m0, m_end, n0, Bp, sBp)) return false;
     m0 = uniform_i64(m0);
     m_end = uniform_i64(m_end);
     n0 = uniform_i64(n0);
@@ -581,10 +670,12 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     return true;
   };
   int64_t tile = blockIdx.x;
-  while (tile < tile_ids && !setup_tile(tile)) tile += gridDim.x;
-  if (tile >= tile_ids) return;
+  while (tile < work_ids && !setup_tile(tile)) tile += gridDim.x;
+  if (tile >= work_ids) return;
 
-  auto issue_load = [&](int kb, int op, uint8_t* st, v8i (&wr)[DNI]) {
+  auto issue_load = [&](int kb, int op, auto stage, v8i (&wr)[DNI]) {
+    lds_u8* st = tile_lds(stage);
+    lds_u8* sc = scl_lds(stage);
     // the per-step part of an address in the vector offset (one add per step,
     // shared by the step's loads), the per-load constant in the scalar offset;
     // the range check sees their sum, as before
@@ -601,18 +692,18 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(reinterpret_cast<const uint8_t*>(sa_tile) + (uint32_t)kb * sa_kbytes), (short)0, rows_m * 4,
           (int)kRsrcWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + kDScaleOff + 256 * (wave & 1)), 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sc + kDScaleOff + 256 * (wave & 1)), 4,
                                                sc_row_off, 0, 0, 0);
     } else if (op == 5) {
       if constexpr (kLayout == kWgrad) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(reinterpret_cast<const uint8_t*>(sb_tile) + (uint32_t)kb * sb_kbytes), (short)0, rows_n * 4,
             (int)kRsrcWord3);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + kDWScaleOff), 16, (uint32_t)(lane * 16), 0, 0,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sc + kDWScaleOff), 16, (uint32_t)(lane * 16), 0, 0,
                                                  0);
       } else {
         // the wave's weight-block scale (every lane fetches the same float)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_sw, (lds_ptr_t)(st + kDWScaleOff + wave * 256), 4,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_sw, (lds_ptr_t)(sc + kDWScaleOff + wave * 256), 4,
                                                  sw_off + (uint32_t)kb * sw_kstride, 0, 0, 0);
       }
     } else {
@@ -666,34 +757,40 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     cl = 0.f;
   };
 
-  auto read_tn = [&](const uint8_t* stn, int half) {
-    const float4 t = *reinterpret_cast<const float4*>(stn + kDScaleOff + lrow * 32 + half * 16);
+  auto read_tn = [&](const uint8_t* scn, int half) {
+    const float4 t = *reinterpret_cast<const float4*>(scn + kDScaleOff + lrow * 32 + half * 16);
     tn[4 * half + 0] = t.x;
     tn[4 * half + 1] = t.y;
     tn[4 * half + 2] = t.z;
     tn[4 * half + 3] = t.w;
   };
-  auto prefetch = [&](const uint8_t* stn) {
-    if constexpr (kBlockW) wn = reinterpret_cast<const float*>(stn + kDWScaleOff)[wave * 64];
-    read_tn(stn, 0);
-    read_tn(stn, 1);
+  auto prefetch = [&](auto stage) {
+    const uint8_t* stn = tile_of(stage);
+    const uint8_t* scn = scl_of(stage);
+    if constexpr (kBlockW) wn = reinterpret_cast<const float*>(scn + kDWScaleOff)[wave * 64];
+    read_tn(scn, 0);
+    read_tn(scn, 1);
     bxa = pair(stn + x_lo, stn + x_hi);
     bxb = pair(stn + x_lo + 2048, stn + x_hi + 2048);
   };
 
-  auto step = [&](auto pad_tag, int kb, const uint8_t* st, v8i (&wc)[DNI], const uint8_t* stn,
-                  uint8_t* sd, v8i (&wf)[DNI]) {
+  auto step = [&](auto pad_tag, int kb, auto s_cur, v8i (&wc)[DNI], auto s_next, auto s_dma,
+                  v8i (&wf)[DNI]) {
+    const uint8_t* st = tile_of(s_cur);
+    const uint8_t* sc = scl_of(s_cur);
+    const uint8_t* stn = tile_of(s_next);
+    const uint8_t* scn = scl_of(s_next);
     constexpr bool kPad = decltype(pad_tag)::value;   // the round may hold padding steps
-    const bool live = !kPad || kb < KB;
-    const int kb_d = kb + 2 < KB ? kb + 2 : KB - 1;   // token tile streamed this step
-    const int kb_w = kb + 3 < KB ? kb + 3 : KB - 1;   // weights streamed this step
+    const bool live = !kPad || kb < kb_hi;
+    const int kb_d = kb + 2 < kb_hi ? kb + 2 : kb_hi - 1;   // token tile streamed this step
+    const int kb_w = kb + 3 < kb_hi ? kb + 3 : kb_hi - 1;   // weights streamed this step
 
     // c[j] (this block's scale of token subtile j) is formed in row j and
     // first used in row j+1
     float c[DNJ];
     float4 rs[DNI];
     if constexpr (kLayout == kWgrad) {
-      const float* swl = reinterpret_cast<const float*>(st + kDWScaleOff);
+      const float* swl = reinterpret_cast<const float*>(sc + kDWScaleOff);
 #pragma unroll
       for (int i = 0; i < DNI; ++i)
         rs[i] = *reinterpret_cast<const float4*>(swl + wave * 64 + i * 16 + lgrp * 4);
@@ -748,7 +845,7 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
         }
         if ((i & 1) && 2 * j + (i >> 1) < kDOpsPerBlock) {
           const int op = 2 * j + (i >> 1);
-          issue_load(op < kDDmaOps ? kb_d : kb_w, op, sd, wf);
+          issue_load(op < kDDmaOps ? kb_d : kb_w, op, s_dma, wf);
         }
         if (j == DNJ - 2) {
           if (i == 0) an_l = *reinterpret_cast<const v4i*>(stn + x_lo);
@@ -759,10 +856,10 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
         if (j == DNJ - 1) {
           // the next block's scales; tn[0..7] are consumed by this step's
           // rows before these reads (c[j] above), so they can be refilled
-          if (i == 0) read_tn(stn, 0);
-          if (i == 1) read_tn(stn, 1);
+          if (i == 0) read_tn(scn, 0);
+          if (i == 1) read_tn(scn, 1);
           if constexpr (kBlockW) {
-            if (i == 2) wn = reinterpret_cast<const float*>(stn + kDWScaleOff)[wave * 64];
+            if (i == 2) wn = reinterpret_cast<const float*>(scn + kDWScaleOff)[wave * 64];
           }
         }
         // instruction order = source order: one MFMA, then the fold of the
@@ -790,25 +887,94 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     }
   };
 
-  // Prologue of a tile, in the steady-state order (weights of block 0; tile
-  // of block 0 and weights of block 1; tile of block 1 and weights of block
-  // 2), blocks past K repeating the last block.  Its wait allows the 22 loads
+  // Prologue of a tile, in the steady-state order (weights of its first
+  // block; tile of the first block and weights of the second; tile of the
+  // second and weights of the third), blocks past the tile's K range
+  // repeating its last block.  Its wait allows the 22 loads
   // issued after block 0's tile (any stores issued after them are younger
   // still), then block 0's first operands are read.  Whole rounds of four
   // steps follow with no conditions inside; when K is not a multiple of four
   // blocks the last round pads with steps that fold with scale 0.
   auto issue_prologue = [&]() {
-    auto clamp = [&](int b) { return b < KB ? b : KB - 1; };
+    auto clamp = [&](int b) { return b < kb_hi ? b : kb_hi - 1; };
 #pragma unroll
-    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(0, op, lds_s0, w0);
+    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(kb_lo, op, S0{}, w0);
 #pragma unroll
-    for (int op = 0; op < kDDmaOps; ++op) issue_load(0, op, lds_s0, w0);
+    for (int op = 0; op < kDDmaOps; ++op) issue_load(kb_lo, op, S0{}, w0);
 #pragma unroll
-    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(1), op, lds_s1, w1);
+    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(kb_lo + 1), op, S1{}, w1);
 #pragma unroll
-    for (int op = 0; op < kDDmaOps; ++op) issue_load(clamp(1), op, lds_s1, w1);
+    for (int op = 0; op < kDDmaOps; ++op) issue_load(clamp(kb_lo + 1), op, S1{}, w1);
 #pragma unroll
-    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(2), op, lds_s2, w2);
+    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(kb_lo + 2), op, S2{}, w2);
+  };
+  // ---- epilogue: lane holds 4 consecutive n of row m for every (i, j) ----
+  auto store_tile = [&](int64_t em0, int64_t em_end, int64_t en0, int erows_m, int erows_n) {
+    if (erows_m == BM && erows_n == BN) {
+      // Full tile: the wave's 64 (n) x 128 (m) block goes through its own
+      // staging area so that every store instruction writes whole row segments
+      // of the output: 8 rows x 128 B (BF16) or 4 rows x 256 B (FP32, in two
+      // halves of 64 rows).  Lane stores of 4 values per row took ~2.5x as
+      // long, all workgroups of a round storing at once.  16-byte chunks are
+      // XOR-swizzled by row.
+      uint8_t* ob = wave == 0 ? lds_z0 : wave == 1 ? lds_z1 : wave == 2 ? lds_z2 : lds_z3;
+      if constexpr (!kOutF32) {
+#pragma unroll
+        for (int j = 0; j < DNJ; ++j) {
+#pragma unroll
+          for (int i = 0; i < DNI; ++i) {
+            const int m = j * 16 + lrow, nl = i * 16 + lgrp * 4;
+            const v4f& r = acc[i][j];
+            const __bf16 h0 = (__bf16)r[0], h1 = (__bf16)r[1], h2 = (__bf16)r[2], h3 = (__bf16)r[3];
+            const uint32_t u0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+            const uint32_t u1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+            *reinterpret_cast<uint2*>(ob + m * 128 + (((nl >> 3) ^ (m & 7)) << 4) + (nl & 7) * 2) =
+                make_uint2(u0, u1);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < BM / 8; ++t) {
+          const int row = t * 8 + (lane >> 3), ch = lane & 7;
+          const uint4 v = *reinterpret_cast<const uint4*>(ob + row * 128 + ((ch ^ (row & 7)) << 4));
+          uint16_t* dst = reinterpret_cast<uint16_t*>(p.C) + (em0 + row) * p.ldc + en0 + wave * 64 + ch * 8;
+          *reinterpret_cast<uint4*>(dst) = v;
+        }
+      } else {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+          for (int j = 0; j < DNJ / 2; ++j) {
+#pragma unroll
+            for (int i = 0; i < DNI; ++i) {
+              const int m = j * 16 + lrow, ch = i * 4 + lgrp;
+              const v4f& r = acc[i][half * (DNJ / 2) + j];
+              *reinterpret_cast<float4*>(ob + m * 256 + ((ch ^ (m & 15)) << 4)) = make_float4(r[0], r[1], r[2], r[3]);
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < BM / 8; ++t) {
+            const int row = t * 4 + (lane >> 4), ch = lane & 15;
+            const float4 v = *reinterpret_cast<const float4*>(ob + row * 256 + ((ch ^ (row & 15)) << 4));
+            float* dst = reinterpret_cast<float*>(p.C) + (em0 + half * (BM / 2) + row) * p.ldc + en0 + wave * 64 + ch * 4;
+            *reinterpret_cast<float4*>(dst) = v;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < DNJ; ++j) {
+        const int64_t m = em0 + j * 16 + lrow;
+        if (m >= em_end) continue;
+#pragma unroll
+        for (int i = 0; i < DNI; ++i) {
+          const int64_t n = en0 + wave * 64 + i * 16 + lgrp * 4;
+          if (n >= p.N) continue;
+          store4<kOutF32>(p, m, n, acc[i][j]);
+        }
+      }
+    }
   };
   zero_state();
   issue_prologue();
@@ -817,22 +983,22 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
-  prefetch(lds_s0);
+  prefetch(S0{});
   using no_pad = std::integral_constant<bool, false>;
   using pad = std::integral_constant<bool, true>;
-  const int KB4 = KB & ~3;
-  int kb = 0;
-  for (; kb < KB4; kb += 4) {
-    step(no_pad{}, kb, lds_s0, w0, lds_s1, lds_s2, w3);
-    step(no_pad{}, kb + 1, lds_s1, w1, lds_s2, lds_s3, w0);
-    step(no_pad{}, kb + 2, lds_s2, w2, lds_s3, lds_s0, w1);
-    step(no_pad{}, kb + 3, lds_s3, w3, lds_s0, lds_s1, w2);
+  const int kb_end4 = kb_lo + ((kb_hi - kb_lo) & ~3);
+  int kb = kb_lo;
+  for (; kb < kb_end4; kb += 4) {
+    step(no_pad{}, kb, S0{}, w0, S1{}, S2{}, w3);
+    step(no_pad{}, kb + 1, S1{}, w1, S2{}, S3{}, w0);
+    step(no_pad{}, kb + 2, S2{}, w2, S3{}, S0{}, w1);
+    step(no_pad{}, kb + 3, S3{}, w3, S0{}, S1{}, w2);
   }
-  if (kb < KB) {
-    step(pad{}, kb, lds_s0, w0, lds_s1, lds_s2, w3);
-    step(pad{}, kb + 1, lds_s1, w1, lds_s2, lds_s3, w0);
-    step(pad{}, kb + 2, lds_s2, w2, lds_s3, lds_s0, w1);
-    step(pad{}, kb + 3, lds_s3, w3, lds_s0, lds_s1, w2);
+  if (kb < kb_hi) {
+    step(pad{}, kb, S0{}, w0, S1{}, S2{}, w3);
+    step(pad{}, kb + 1, S1{}, w1, S2{}, S3{}, w0);
+    step(pad{}, kb + 2, S2{}, w2, S3{}, S0{}, w1);
+    step(pad{}, kb + 3, S3{}, w3, S0{}, S1{}, w2);
   }
   if constexpr (kBlockW) {
 #pragma unroll
@@ -848,81 +1014,124 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   __asm__ volatile("" ::: "memory");
   const int64_t em0 = m0, em_end = m_end, en0 = n0;
   const int erows_m = rows_m, erows_n = rows_n;
+  const int epiece = piece_slot;
   int64_t next = tile + gridDim.x;
-  while (next < tile_ids && !setup_tile(next)) next += gridDim.x;
-  const bool more = next < tile_ids;
+  while (next < work_ids && !setup_tile(next)) next += gridDim.x;
+  const bool more = next < work_ids;
   if (more) issue_prologue();
-  // ---- epilogue: lane holds 4 consecutive n of row m for every (i, j) ----
-  if (erows_m == BM && erows_n == BN) {
-    // Full tile: the wave's 64 (n) x 128 (m) block goes through its own
-    // staging area so that every store instruction writes whole row segments
-    // of the output: 8 rows x 128 B (BF16) or 4 rows x 256 B (FP32, in two
-    // halves of 64 rows).  Lane stores of 4 values per row took ~2.5x as
-    // long, all workgroups of a round storing at once.  16-byte chunks are
-    // XOR-swizzled by row.
-    uint8_t* ob = lds_out[wave];
-    if constexpr (!kOutF32) {
+  if (epiece >= 0) {
+    // A K piece of a split tile (a workgroup's last work item).  Its FP32
+    // partial tile goes to the workspace in fragment order (16 B per lane per
+    // (i, j): 1 KB per wave per store); then the tile's counter counts it.
+    // The piece that arrives last adds the tile's partials in piece order -
+    // a fixed order, so the result does not depend on which piece that is -
+    // zeroes the counter for the next launch, and stores the tile.
+    constexpr int kWaveF4 = DNI * DNJ * 64;
+    constexpr int64_t kTileF4 = kSplitTileFloats / 4;
+    float4* part = reinterpret_cast<float4*>(p.ws_partial) + (int64_t)epiece * kTileF4 + wave * kWaveF4 + lane;
+#pragma unroll
+    for (int i = 0; i < DNI; ++i)
+#pragma unroll
+      for (int j = 0; j < DNJ; ++j)
+        part[(i * DNJ + j) * 64] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    // Release: each wave's partial stores are complete (acknowledged by its
+    // XCD's L2) before the barrier - a workgroup barrier alone does not wait
+    // for them - then one lane writes that L2's dirty lines back (so the
+    // other XCDs see them) and counts the piece.  One fence per piece, not
+    // one per wave: each writes back the whole L2.
+    wait_vm_lgkm0<0>();
+    __syncthreads();
+    // the arrival count passes through unused bytes of stage 0 (no DMA is
+    // in flight: a piece is its workgroup's last work item; a separate LDS
+    // object would move the stages past the 64 KB reach of LDS offsets)
+    uint32_t* arrive = reinterpret_cast<uint32_t*>(lds_c0 + kDFreeOff);
+    const int et = epiece / plan.split;
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      *arrive = atomicAdd(&p.ws_count[et], 1u);
+    }
+    __syncthreads();
+    if (*arrive != (uint32_t)(plan.split - 1)) return;
+    // Acquire, by the wave that read the final count: drop stale lines from
+    // the CU's L1 and the XCD's L2, which the whole workgroup shares, before
+    // any wave reads the other pieces' partials
+    if (wave == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
+    // partial 0, then partials 1.. added in turn, each read as one batch of
+    // 32 independent 16-byte loads per lane
+    const float4* first = reinterpret_cast<const float4*>(p.ws_partial) + (int64_t)et * plan.split * kTileF4 +
+                          wave * kWaveF4 + lane;
+#pragma unroll
+    for (int i = 0; i < DNI; ++i)
 #pragma unroll
       for (int j = 0; j < DNJ; ++j) {
-#pragma unroll
-        for (int i = 0; i < DNI; ++i) {
-          const int m = j * 16 + lrow, nl = i * 16 + lgrp * 4;
-          const v4f& r = acc[i][j];
-          const __bf16 h0 = (__bf16)r[0], h1 = (__bf16)r[1], h2 = (__bf16)r[2], h3 = (__bf16)r[3];
-          const uint32_t u0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                              ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-          const uint32_t u1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
-                              ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-          *reinterpret_cast<uint2*>(ob + m * 128 + (((nl >> 3) ^ (m & 7)) << 4) + (nl & 7) * 2) =
-              make_uint2(u0, u1);
-        }
+        const float4 u = first[(i * DNJ + j) * 64];
+        acc[i][j] = v4f{u.x, u.y, u.z, u.w};
       }
+    for (int q = 1; q < plan.split; ++q) {
+      const float4* src = first + (int64_t)q * kTileF4;
+      float4 u[DNI][DNJ];
 #pragma unroll
-      for (int t = 0; t < BM / 8; ++t) {
-        const int row = t * 8 + (lane >> 3), ch = lane & 7;
-        const uint4 v = *reinterpret_cast<const uint4*>(ob + row * 128 + ((ch ^ (row & 7)) << 4));
-        uint16_t* dst = reinterpret_cast<uint16_t*>(p.C) + (em0 + row) * p.ldc + en0 + wave * 64 + ch * 8;
-        *reinterpret_cast<uint4*>(dst) = v;
-      }
-    } else {
+      for (int i = 0; i < DNI; ++i)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+        for (int j = 0; j < DNJ; ++j) u[i][j] = src[(i * DNJ + j) * 64];
 #pragma unroll
-        for (int j = 0; j < DNJ / 2; ++j) {
+      for (int i = 0; i < DNI; ++i)
 #pragma unroll
-          for (int i = 0; i < DNI; ++i) {
-            const int m = j * 16 + lrow, ch = i * 4 + lgrp;
-            const v4f& r = acc[i][half * (DNJ / 2) + j];
-            *reinterpret_cast<float4*>(ob + m * 256 + ((ch ^ (m & 15)) << 4)) = make_float4(r[0], r[1], r[2], r[3]);
-          }
+        for (int j = 0; j < DNJ; ++j) {
+          acc[i][j][0] += u[i][j].x;
+          acc[i][j][1] += u[i][j].y;
+          acc[i][j][2] += u[i][j].z;
+          acc[i][j][3] += u[i][j].w;
         }
-#pragma unroll
-        for (int t = 0; t < BM / 8; ++t) {
-          const int row = t * 4 + (lane >> 4), ch = lane & 15;
-          const float4 v = *reinterpret_cast<const float4*>(ob + row * 256 + ((ch ^ (row & 15)) << 4));
-          float* dst = reinterpret_cast<float*>(p.C) + (em0 + half * (BM / 2) + row) * p.ldc + en0 + wave * 64 + ch * 4;
-          *reinterpret_cast<float4*>(dst) = v;
-        }
-      }
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < DNJ; ++j) {
-      const int64_t m = em0 + j * 16 + lrow;
-      if (m >= em_end) continue;
-#pragma unroll
-      for (int i = 0; i < DNI; ++i) {
-        const int64_t n = en0 + wave * 64 + i * 16 + lgrp * 4;
-        if (n >= p.N) continue;
-        store4<kOutF32>(p, m, n, acc[i][j]);
-      }
-    }
+    if (tid == 0) p.ws_count[et] = 0u;
+    // the split path ends here and never reaches the K loop again (the
+    // compiler's wait analysis would otherwise carry its loads into the loop)
+    store_tile(em0, em_end, en0, erows_m, erows_n);
+    return;
   }
+  store_tile(em0, em_end, en0, erows_m, erows_n);
   if (!more) break;
   tile = next;
   zero_state();
   }
 }
+
+template <int kLayout, bool kGrouped>
+hipError_t launch_typed(const GemmProblem& p, hipStream_t stream, int64_t grid, int64_t total) {
+  if constexpr (kLayout == kDgrad) {
+    if (p.out_fp32) {
+      hipLaunchKernelGGL((block_gemm_kernel<kLayout, true, kGrouped>), dim3((unsigned)grid),
+                         dim3(kThreads), 0, stream, p, total);
+    } else {
+      hipLaunchKernelGGL((block_gemm_kernel<kLayout, false, kGrouped>), dim3((unsigned)grid),
+                         dim3(kThreads), 0, stream, p, total);
+    }
+  } else {
+    grid = persistent_grid(grid);
+    if (p.b_tiled) {
+      if (p.out_fp32) {
+        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped, true>), dim3((unsigned)grid),
+                           dim3(kThreads), 0, stream, p, total);
+      } else {
+        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped, true>), dim3((unsigned)grid),
+                           dim3(kThreads), 0, stream, p, total);
+      }
+    } else {
+      if (p.out_fp32) {
+        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped, false>), dim3((unsigned)grid),
+                           dim3(kThreads), 0, stream, p, total);
+      } else {
+        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped, false>), dim3((unsigned)grid),
+                           dim3(kThreads), 0, stream, p, total);
+      }
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
 
 // Compute units of the current device (cached); 0 if unknown.
 int device_cus() {
@@ -943,44 +1152,13 @@ int device_cus() {
   return n;
 }
 
-template <int kLayout, bool kGrouped>
-hipError_t launch_typed(const GemmProblem& p, hipStream_t stream, int64_t grid, int64_t total) {
-  if constexpr (kLayout == kDgrad) {
-    if (p.out_fp32) {
-      hipLaunchKernelGGL((block_gemm_kernel<kLayout, true, kGrouped>), dim3((unsigned)grid),
-                         dim3(kThreads), 0, stream, p, total);
-    } else {
-      hipLaunchKernelGGL((block_gemm_kernel<kLayout, false, kGrouped>), dim3((unsigned)grid),
-                         dim3(kThreads), 0, stream, p, total);
-    }
-  } else {
-    // persistent: one workgroup per CU (the LDS footprint allows no second
-    // one), a multiple of 8 so each workgroup stays on one XCD's tile run
-    const int64_t ids = grid;
-    const int cus = device_cus();
-    if (cus >= 8 && grid > cus) grid = cus / 8 * 8;
-    if (p.b_tiled) {
-      if (p.out_fp32) {
-        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped, true>), dim3((unsigned)grid),
-                           dim3(kThreads), 0, stream, p, total, ids);
-      } else {
-        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped, true>), dim3((unsigned)grid),
-                           dim3(kThreads), 0, stream, p, total, ids);
-      }
-    } else {
-      if (p.out_fp32) {
-        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, true, kGrouped, false>), dim3((unsigned)grid),
-                           dim3(kThreads), 0, stream, p, total, ids);
-      } else {
-        hipLaunchKernelGGL((block_gemm_direct_kernel<kLayout, false, kGrouped, false>), dim3((unsigned)grid),
-                           dim3(kThreads), 0, stream, p, total, ids);
-      }
-    }
-  }
-  return hipGetLastError();
+// Workgroups of a persistent direct-kernel launch over `ids` tiles: one per
+// CU (the LDS footprint allows no second one), a multiple of 8 so that each
+// workgroup stays on one XCD's tile run; one per tile when there are fewer.
+int64_t persistent_grid(int64_t ids) {
+  const int cus = device_cus();
+  return (cus >= 8 && ids > cus) ? cus / 8 * 8 : ids;
 }
-
-}  // namespace
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
   const int64_t tiles_n = (p.N + BN - 1) / BN;

@@ -74,9 +74,65 @@ struct GemmProblem {
   // grouped FPROP: groups > 0
   int groups;
   const int32_t* offsets;
+  // split-K workspace of the persistent kernel (null: no split): ws_slots
+  // partial tiles of kSplitTileFloats floats, then ws_slots counters that
+  // are zero between launches
+  float* ws_partial;
+  uint32_t* ws_count;
+  int64_t ws_slots;
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+// compute units of the current device (cached); 0 if unknown
+int device_cus();
+// workgroups of a persistent GEMM launch over `ids` tiles
+int64_t persistent_grid(int64_t ids);
+
+// ---- split-K tail of the persistent GEMM ----
+// FP32 partial sums of one 128 x 256 output tile
+constexpr int64_t kSplitTileFloats = 128 * 256;
+constexpr int kMaxSplit = 16;
+// Workspace bytes for `slots` pieces: the partial tiles, then the counters.
+inline size_t split_workspace_bytes(int64_t slots) {
+  return (size_t)slots * (size_t)kSplitTileFloats * 4u + (size_t)slots * 4u;
+}
+
+// How a persistent launch of `grid` workgroups covers `tiles` output tiles
+// of `kb` K blocks.  Whole rounds of one tile per workgroup come first
+// (dp_tiles tiles).  When the leftover tiles would fill at most half of a
+// last round, each of them is cut along K into `split` pieces of whole
+// 4-block rounds, run by the workgroups that would otherwise idle; the
+// fewest pieces that reach the shortest piece length are taken, since every
+// extra piece adds a partial tile to the final sum.  split == 1: no split.
+struct SplitPlan {
+  int64_t dp_tiles;      // tiles run whole
+  int64_t split_tiles;   // tiles run as `split` pieces each (tile ids dp_tiles..)
+  int split;
+  int rounds;            // 4-block rounds of K
+};
+__host__ __device__ inline SplitPlan split_plan(int64_t tiles, int64_t grid, int kb, int64_t slots) {
+  SplitPlan s{tiles, 0, 1, (kb + 3) / 4};
+  if (grid <= 0 || tiles <= grid || slots <= 0) return s;
+  const int64_t left = tiles % grid;
+  if (left == 0) return s;
+  int64_t most = grid / left;
+  if (most > kMaxSplit) most = kMaxSplit;
+  if (most > s.rounds) most = s.rounds;
+  if (most < 2) return s;
+  const int64_t per = (s.rounds + most - 1) / most;      // rounds per piece at the most pieces
+  const int64_t pieces = (s.rounds + per - 1) / per;     // the fewest pieces of that length
+  if (pieces < 2 || left * pieces > slots) return s;
+  s.dp_tiles = tiles - left;
+  s.split_tiles = left;
+  s.split = (int)pieces;
+  return s;
+}
+// K blocks [lo, hi) of piece `piece` of a split tile
+__host__ __device__ inline void split_range(const SplitPlan& s, int piece, int kb, int& lo, int& hi) {
+  lo = 4 * (int)((int64_t)piece * s.rounds / s.split);
+  hi = 4 * (int)((int64_t)(piece + 1) * s.rounds / s.split);
+  if (hi > kb) hi = kb;
+}
 
 // Fprop with the 1x128 quantization of X fused in (BF16 X in).
 struct FusedFpropProblem {

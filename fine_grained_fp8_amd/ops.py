@@ -7,6 +7,8 @@ ld = round_up(rows, 4) for 1x128 row tiles.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -370,6 +372,19 @@ def probe_recip_online(s: torch.Tensor, *, stream=None):
     st = lib.fp8_probe_recip_online(_ptr(s), _ptr(r), s.numel(), _stream(stream))
     _lib.check("fp8_probe_recip_online", st)
     return r
+
+
+def probe_gemm_split(tiles: int, K: int, *, stream=None):
+    """Measurement aid: (split_tiles, pieces) - how the persistent GEMM kernel
+    schedules `tiles` output tiles of 128 x 256 with K-dimension K on `stream`:
+    the number of leftover tiles cut along K and the pieces per such tile
+    (0, 1: whole tiles only)."""
+    lib = _lib.load_library()
+    n = ctypes.c_int64(0)
+    k = ctypes.c_int32(0)
+    st = lib.fp8_probe_gemm_split(tiles, K, _stream(stream), ctypes.byref(n), ctypes.byref(k))
+    _lib.check("fp8_probe_gemm_split", st)
+    return n.value, k.value
 
 
 def quant_act_tiles(x: torch.Tensor, tile: int = 128, rank: int = 1, *, sat_count=None, stream=None):

@@ -5,6 +5,7 @@
  * GEMM.  These calls exist so that a roofline can be put beside the GEMMs'
  * measured rate (the matrix unit's sustained rate with no memory traffic) and
  * so that a step of the quantizers' arithmetic can be checked exhaustively.
+ * The split query reports how the GEMM kernel schedules a launch.
  * They follow the conventions of fp8bs.h: caller-owned device buffers,
  * host-side validation before any launch, asynchronous on `stream`, and an
  * fp8_status result.
@@ -60,6 +61,24 @@ fp8_status fp8_probe_mfma(int64_t workgroups, int32_t iters, int32_t mode, const
  *  FP8_ERR_DEVICE, FP8_ERR_LAUNCH.
  */
 fp8_status fp8_probe_recip_online(const float* s, float* r, int64_t n, void* stream);
+
+/*
+ * fp8_probe_gemm_split - the schedule the persistent GEMM kernel (FPROP,
+ * DGRAD_T, WGRAD, grouped) takes for `tiles` output tiles of 128 x 256 with
+ * K-dimension `K` when enqueued on `stream` of the current device, so that a
+ * test can tell whether a launch ran the split-K tail it means to check.
+ * When the tiles leave the last round of one tile per workgroup at most half
+ * full, each leftover tile is cut along K into pieces run by otherwise idle
+ * workgroups, the last piece to finish adding the partial tiles in piece
+ * order; that needs the split workspace the library holds per stream (made by
+ * the first GEMM call on the stream).
+ *  tiles        >= 0
+ *  K            > 0, a multiple of 128
+ *  split_tiles  host: receives the number of tiles run as pieces (0: none)
+ *  pieces       host: receives the pieces per split tile (1: no split)
+ *  Errors: FP8_ERR_SHAPE, FP8_ERR_NULL, FP8_ERR_DEVICE.
+ */
+fp8_status fp8_probe_gemm_split(int64_t tiles, int64_t K, void* stream, int64_t* split_tiles, int32_t* pieces);
 
 #ifdef __cplusplus
 }

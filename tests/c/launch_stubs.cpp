@@ -35,5 +35,7 @@ hipError_t launch_mfma_probe(int64_t, int, int, const uint8_t*, float*, hipStrea
 hipError_t launch_recip_online_probe(const float*, float*, int64_t, hipStream_t) { FP8BS_STUB; }
 hipError_t launch_gemm(const GemmProblem&, hipStream_t) { FP8BS_STUB; }
 hipError_t launch_fused_quant_fprop(const FusedFpropProblem&, hipStream_t) { FP8BS_STUB; }
+int device_cus() { return 0; }
+int64_t persistent_grid(int64_t ids) { return ids; }
 
 }  // namespace fp8bs

@@ -291,6 +291,21 @@ def test_probe_mfma_validation(lib):
     assert f() in (DEVICE, OK)
 
 
+def test_probe_gemm_split_validation(lib):
+    import ctypes
+    n, k = ctypes.c_int64(-5), ctypes.c_int32(-5)
+    f = lambda tiles=300, K=1024, a=ctypes.byref(n), b=ctypes.byref(k): lib.fp8_probe_gemm_split(tiles, K, None, a, b)
+    assert f(tiles=-1) == SHAPE
+    assert f(K=0) == SHAPE
+    assert f(K=1000) == SHAPE
+    assert f(a=None) == NULL
+    assert f(b=None) == NULL
+    st = f()
+    assert st in (DEVICE, OK)
+    if st == OK:   # no GEMM ran on this stream: no split workspace, whole tiles only
+        assert (n.value, k.value) == (0, 1)
+
+
 def test_gemm_promotion_validation(lib):
     f = lambda A_=A, M=64, K=256, lda=256, B_=B, N=48, ldb=256, pk=128, C_=C, ldc=48: \
         lib.fp8_gemm_promotion(A_, M, K, lda, B_, N, ldb, pk, C_, ldc, None)

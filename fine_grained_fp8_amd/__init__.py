@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     quant_act_dual,
     quant_weight_128x128,
     block_gemm,
+    block_gemm_noalloc,
     block_gemm_fused_quant,
     block_gemm_grouped,
     amax_history_update,
@@ -30,6 +31,6 @@ from .ops import (  # noqa: F401
 
 __all__ = [
     "FP8Error", "load_library", "quant_act_1x128", "quant_act_dual", "quant_weight_128x128", "block_gemm",
-    "block_gemm_fused_quant", "block_gemm_grouped", "amax_history_update", "cast_e4m3", "message_bytes", "pack_tokens",
+    "block_gemm_noalloc", "block_gemm_fused_quant", "block_gemm_grouped", "amax_history_update", "cast_e4m3", "message_bytes", "pack_tokens",
     "unpack_tokens", "dequant_tokens", "gemm_promotion", "quant_act_tiles", "probe_mfma", "probe_recip_online", "probe_gemm_split", "round_up",
 ]

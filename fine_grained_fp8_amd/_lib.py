@@ -35,6 +35,8 @@ SIGNATURES = {
     "fp8_quant_weight_128x128": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
     "fp8_block_gemm": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P,
                                       _I64, _P, ctypes.c_int, _I64, _P]),
+    "fp8_block_gemm_noalloc": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64,
+                                              _P, _I64, _P, ctypes.c_int, _I64, _P]),
     "fp8_quant_weight_128x128_tiled": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _I64, _P]),
     "fp8_block_gemm_grouped_tiled": (ctypes.c_int, [_I32, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P,
                                                     _P, _P, ctypes.c_int, _I64, _P]),

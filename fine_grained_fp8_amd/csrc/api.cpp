@@ -458,10 +458,11 @@ static fp8_status validate_gemm_common(int64_t M, int64_t N, int64_t K, const ui
   return FP8_OK;
 }
 
-fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t K,
-                          const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
-                          const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
-                          void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream) {
+namespace {
+fp8_status block_gemm_impl(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t K,
+                           const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
+                           const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
+                           void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream, bool noalloc) {
   if (layout != FP8_LAYOUT_FPROP && layout != FP8_LAYOUT_DGRAD && layout != FP8_LAYOUT_WGRAD &&
       layout != FP8_LAYOUT_DGRAD_T && layout != FP8_LAYOUT_FPROP_TILED &&
       layout != FP8_LAYOUT_DGRAD_T_TILED && layout != FP8_LAYOUT_WGRAD_TILED)
@@ -505,8 +506,32 @@ fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t 
   p.C = C; p.ldc = ldc; p.out_fp32 = c_dtype == FP8_OUT_FP32;
   p.b_tiled = tiled ? 1 : 0;
   p.groups = 0; p.offsets = nullptr;
-  attach_workspace(p, reinterpret_cast<hipStream_t>(stream));
+  if (noalloc) {
+    // the static workspace holds one piece per CU of up to kStaticSlots CUs
+    if (fp8bs::device_cus() > fp8bs::kStaticSlots) return FP8_ERR_UNSUPPORTED;
+    if (fp8bs::attach_static_workspace(p, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) {
+      (void)hipGetLastError();
+      return FP8_ERR_LAUNCH;
+    }
+  } else {
+    attach_workspace(p, reinterpret_cast<hipStream_t>(stream));
+  }
   return launched(fp8bs::launch_gemm(p, reinterpret_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t K,
+                          const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
+                          const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
+                          void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream) {
+  return block_gemm_impl(layout, M, N, K, A, lda, sA, ld_sa, B, ldb, sB, ld_sb, C, c_dtype, ldc, stream, false);
+}
+
+fp8_status fp8_block_gemm_noalloc(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t K,
+                                  const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
+                                  const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
+                                  void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream) {
+  return block_gemm_impl(layout, M, N, K, A, lda, sA, ld_sa, B, ldb, sB, ld_sb, C, c_dtype, ldc, stream, true);
 }
 
 fp8_status fp8_block_gemm_fused_quant(int64_t M, int64_t N, int64_t K, const void* x, int64_t ldx,

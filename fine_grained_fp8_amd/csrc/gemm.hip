@@ -43,6 +43,7 @@
 //  * Tile ids are remapped so each XCD (ids congruent mod 8) walks a
 //    contiguous, M-grouped run of tiles and its private L2 sees the reuse.
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "device.hpp"
@@ -1158,6 +1159,50 @@ int device_cus() {
 int64_t persistent_grid(int64_t ids) {
   const int cus = device_cus();
   return (cus >= 8 && ids > cus) ? cus / 8 * 8 : ids;
+}
+
+// ---- split workspace for callers that cannot allocate ----
+// One partial tile per piece for kStaticSlots pieces (one per CU of a
+// device with up to kStaticSlots CUs), then the per-tile counters: 32 MB +
+// 1 KB, held by every GPU the library runs on until the process ends.  In
+// host code `scratch` only stands for the symbol; its device address comes
+// from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kStaticSlots * kSplitTileFloats * 4 + kStaticSlots * 4];
+
+__global__ void zero_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t attach_static_workspace(GemmProblem& p, hipStream_t stream) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* base[kMaxDev];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  const size_t count_off = (size_t)kStaticSlots * (size_t)kSplitTileFloats * 4u;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (base[dev] == nullptr) {
+      void* ptr = nullptr;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      // the counters start at zero (each launch leaves them zero); cleared
+      // by a kernel, not a memset, so that a capturing caller records a
+      // kernel node
+      hipLaunchKernelGGL(zero_words, dim3(1), dim3(kStaticSlots), 0, stream,
+                         reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ptr) + count_off), (int)kStaticSlots);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      base[dev] = ptr;
+    }
+    p.ws_partial = static_cast<float*>(base[dev]);
+    p.ws_count = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(base[dev]) + count_off);
+    p.ws_slots = kStaticSlots;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {

@@ -97,6 +97,13 @@ inline size_t split_workspace_bytes(int64_t slots) {
   return (size_t)slots * (size_t)kSplitTileFloats * 4u + (size_t)slots * 4u;
 }
 
+// pieces the static split workspace holds (one per CU up to this count)
+constexpr int64_t kStaticSlots = 256;
+// Point p's split workspace at the library's static array on the current
+// device (found once per device; its counters cleared by a kernel on
+// `stream` then).  Allocates nothing.
+hipError_t attach_static_workspace(GemmProblem& p, hipStream_t stream);
+
 // How a persistent launch of `grid` workgroups covers `tiles` output tiles
 // of `kb` K blocks.  Whole rounds of one tile per workgroup come first
 // (dp_tiles tiles).  When the leftover tiles would fill at most half of a

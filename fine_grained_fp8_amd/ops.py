@@ -144,8 +144,17 @@ def quant_weight_128x128(w: torch.Tensor, *, transposed: bool = False, tiled: bo
     return q, scales, q_t
 
 
+def block_gemm_noalloc(layout: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor,
+                       *, out, stream=None):
+    """block_gemm through fp8_block_gemm_noalloc: the library allocates
+    nothing (its split workspace is a static device array shared by every call
+    on the GPU; calls that overlap in time on one GPU race).  `out` is the
+    caller's C [M][N] (bfloat16 or float32)."""
+    return block_gemm(layout, A, sA, B, sB, out=out, stream=stream, _entry="fp8_block_gemm_noalloc")
+
+
 def block_gemm(layout: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor,
-               *, out_dtype=torch.bfloat16, out=None, stream=None):
+               *, out_dtype=torch.bfloat16, out=None, stream=None, _entry="fp8_block_gemm"):
     """Block-scaled FP8 GEMM.
 
     fprop: A [M][K], sA [K/128][>=M], B [N][K], sB [N/128][>=K/128]
@@ -169,11 +178,11 @@ def block_gemm(layout: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, 
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=A.device)
     code = _lib.OUT_FP32 if out.dtype == torch.float32 else _lib.OUT_BF16
-    st = lib.fp8_block_gemm(
+    st = getattr(lib, _entry)(
         _lib.LAYOUT[layout], M, N, K, _ptr(A), A.stride(0), _ptr(sA), sA.stride(0),
         _ptr(B), B.stride(0), _ptr(sB), sB.stride(0), _ptr(out), code, out.stride(0),
         _stream(stream))
-    _lib.check("fp8_block_gemm", st)
+    _lib.check(_entry, st)
     return out
 
 

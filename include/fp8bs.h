@@ -226,11 +226,41 @@ fp8_status fp8_quant_weight_128x128_tiled(const void* w, int64_t rows, int64_t c
  *  M == 0 is a no-op.  C must not overlap A, B or the scales.
  *  Limits (FP8_ERR_UNSUPPORTED beyond them): lda, ldb <= 2^23, and each
  *  scale table (its rows x ld x 4 bytes) under 2 GiB.
+ *  Workspace: FPROP, DGRAD_T and WGRAD run on a persistent grid of one
+ *  workgroup per CU.  When the output tiles leave that grid's last round at
+ *  most half full, the leftover tiles are cut along K and their FP32 partial
+ *  sums added in a fixed order (the result is deterministic and within the
+ *  same tolerance; it can differ from the whole-tile sum in the last bits).
+ *  The partial sums live in a workspace the library allocates on the first
+ *  call on `stream` (128 KB per CU plus 4 bytes per CU, kept until the
+ *  process ends, one per stream and device); without one - the stream is
+ *  being captured into a graph, or the allocation fails - whole tiles run.
  */
 fp8_status fp8_block_gemm(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t K,
                           const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
                           const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
                           void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream);
+
+/*
+ * fp8_block_gemm_noalloc - fp8_block_gemm for callers that cannot allocate
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, kernels and results, with the split
+ * workspace in a static device array of the library instead of an
+ * allocation.  The call allocates nothing, on the device or the host.
+ *  The array holds 256 pieces (one per CU): 32 MiB + 1 KiB on every GPU the
+ *  library runs on, kept until the process ends.  Devices with more than
+ *  256 CUs are refused (FP8_ERR_UNSUPPORTED).
+ *  All calls on one GPU share the array: calls that overlap in time on one
+ *  GPU (different streams, not ordered) race and give wrong results; calls
+ *  on one stream are ordered and safe.  The array keeps the last call's
+ *  partial sums; its counters return to zero after every launch and are
+ *  cleared once per device by a kernel on `stream` at the first call.
+ *  Errors: as fp8_block_gemm, plus FP8_ERR_UNSUPPORTED above.
+ */
+fp8_status fp8_block_gemm_noalloc(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t K,
+                                  const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
+                                  const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
+                                  void* C, fp8_out_dtype c_dtype, int64_t ldc, void* stream);
 
 /*
  * fp8_block_gemm_fused_quant - FPROP with the 1x128 quantization of X fused
@@ -267,13 +297,15 @@ fp8_status fp8_block_gemm_fused_quant(int64_t M, int64_t N, int64_t K, const voi
  *               g covers rows [lo, hi) with lo = min(max(offsets[g], 0),
  *               total_M) and hi = min(max(offsets[g+1], lo), total_M), so a
  *               decreasing pair gives an empty group.  For an array that
- *               breaks the contract the values of C are unspecified (clamped
- *               groups may overlap, and rows past the launch's tile budget
- *               stay unwritten), but C is never written outside those rows.
+ *               breaks the contract the values of C are unspecified
+ *               (clamped groups may overlap), but C is never written
+ *               outside those rows.
  *  A   X_q [total_M][lda >= K];  sA [K/128][ld_sa >= total_M]
  *  B   W_q [groups][N][ldb >= K] (group g at B + g * N * ldb)
  *  sB  [groups][N/128][K/128] contiguous
  *  C   [total_M][ldc >= N], BF16 or FP32.   N % 128 == 0, K % 128 == 0.
+ *  The tiles are counted on the device from the offsets; the split of
+ *  leftover tiles and its per-stream workspace are as for fp8_block_gemm.
  */
 fp8_status fp8_block_gemm_grouped(int32_t groups, const int32_t* offsets_dev, int64_t total_M,
                                   int64_t N, int64_t K, const uint8_t* A, int64_t lda,

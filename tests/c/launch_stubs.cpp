@@ -36,6 +36,7 @@ hipError_t launch_recip_online_probe(const float*, float*, int64_t, hipStream_t)
 hipError_t launch_gemm(const GemmProblem&, hipStream_t) { FP8BS_STUB; }
 hipError_t launch_fused_quant_fprop(const FusedFpropProblem&, hipStream_t) { FP8BS_STUB; }
 int device_cus() { return 0; }
+hipError_t attach_static_workspace(GemmProblem&, hipStream_t) { FP8BS_STUB; }
 int64_t persistent_grid(int64_t ids) { return ids; }
 
 }  // namespace fp8bs

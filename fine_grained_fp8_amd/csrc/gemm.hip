@@ -584,9 +584,27 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   // them are the K pieces of the leftover tiles, one per workgroup, summed by
   // the piece that finishes last.
   const int KB = (int)(p.K / BK);
-  const int64_t n_tiles = kGrouped ? uniform_i64(grouped_tile_count(p)) : total_tiles;
-  const SplitPlan plan = split_plan(n_tiles, gridDim.x, KB, p.ws_partial != nullptr ? p.ws_slots : 0);
-  const int64_t work_ids = plan.dp_tiles + plan.split_tiles * plan.split;
+  // The schedule sits in LDS (stage 2's free scale bytes, one copy per wave)
+  // and is read back at each tile boundary: registers held across the K loop
+  // are scarce, and a grouped launch's extra state would otherwise spill.
+  struct PlanLds {
+    int64_t dp_tiles, split_tiles, work_ids;
+    int32_t split, rounds;
+  };
+  static_assert(4 * sizeof(PlanLds) <= kDWScaleOff - kDFreeOff, "schedule fits the free scale bytes");
+  PlanLds* plan_lds = reinterpret_cast<PlanLds*>(lds_c2 + kDFreeOff) + wave;
+  {
+    const int64_t n_tiles = kGrouped ? uniform_i64(grouped_tile_count(p)) : total_tiles;
+    const SplitPlan pl = split_plan(n_tiles, gridDim.x, KB, p.ws_partial != nullptr ? p.ws_slots : 0);
+    if (lane == 0)
+      *plan_lds = PlanLds{pl.dp_tiles, pl.split_tiles, pl.dp_tiles + pl.split_tiles * pl.split, pl.split, pl.rounds};
+  }
+  auto load_plan = [&](int64_t& work_ids) -> SplitPlan {
+    const PlanLds v = *plan_lds;
+    work_ids = uniform_i64(v.work_ids);
+    return SplitPlan{uniform_i64(v.dp_tiles), uniform_i64(v.split_tiles), __builtin_amdgcn_readfirstlane(v.split),
+                     __builtin_amdgcn_readfirstlane(v.rounds)};
+  };
   int kb_lo = 0, kb_hi = KB;        // the tile's K blocks
   int piece_slot = -1;              // split piece: its workspace slot; -1: a whole tile
   constexpr bool kBlockW = kLayout == kFprop || kLayout == kDgradT;
@@ -630,6 +648,8 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   // decode work id `id` and set up its buffer resources; false if it names
   // no tile
   auto setup_tile = [&](int64_t id) -> bool {
+    int64_t work_ids;
+    const SplitPlan plan = load_plan(work_ids);
     int64_t b;
     if (id < plan.dp_tiles) {
       b = xcd_remap(id, plan.dp_tiles);
@@ -671,8 +691,12 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     return true;
   };
   int64_t tile = blockIdx.x;
-  while (tile < work_ids && !setup_tile(tile)) tile += gridDim.x;
-  if (tile >= work_ids) return;
+  {
+    int64_t work_ids;
+    (void)load_plan(work_ids);
+    while (tile < work_ids && !setup_tile(tile)) tile += gridDim.x;
+    if (tile >= work_ids) return;
+  }
 
   auto issue_load = [&](int kb, int op, auto stage, v8i (&wr)[DNI]) {
     lds_u8* st = tile_lds(stage);
@@ -1017,6 +1041,8 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   const int erows_m = rows_m, erows_n = rows_n;
   const int epiece = piece_slot;
   int64_t next = tile + gridDim.x;
+  int64_t work_ids;
+  const SplitPlan plan = load_plan(work_ids);
   while (next < work_ids && !setup_tile(next)) next += gridDim.x;
   const bool more = next < work_ids;
   if (more) issue_prologue();

@@ -200,11 +200,10 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
       vals[i] = val;
     }
   };
-  // A workgroup takes blocks blockIdx.x, blockIdx.x + gridDim.x, ...; the
-  // next block's loads fly while this block is reduced and stored.
-  int64_t blk = blockIdx.x;
-  if (blk < nblocks) load_block(blk);
-  for (; blk < nblocks; blk += gridDim.x) {
+  // A workgroup takes blocks blockIdx.x, blockIdx.x + gridDim.x, ... (one
+  // block each at the launch's grid; no registers held for a prefetch)
+  for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+    load_block(blk);
     const int64_t rb = blk / ncb;
     const int64_t c0 = (blk % ncb) * 64;
     const int64_t r0 = rb * 128;
@@ -214,7 +213,6 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
       const int row = ci >> 3, cc = ci & 7;
       *reinterpret_cast<uint4*>(&tile[cols_tile_word(row, cc * 4)]) = vals[i];
     }
-    if (blk + gridDim.x < nblocks) load_block(blk + gridDim.x);
     __syncthreads();
     const int lane = t & 63, g = lane & 7;
     const int p = 8 * (t >> 6) + (lane >> 3);
@@ -279,7 +277,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
 // column quantizers produce.
 // ---------------------------------------------------------------------------
 template <bool kTiled>
-__global__ __launch_bounds__(256) void quant_dual_kernel(
+__global__ __launch_bounds__(256, 5) void quant_dual_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t ncb, int64_t nbr, int64_t nblocks,
     uint8_t* __restrict__ q_row, int64_t ldq_row, float* __restrict__ s_row, int64_t ld_s_row,
     uint8_t* __restrict__ q_col, int64_t ldq_col, float* __restrict__ s_col, int64_t ld_s_col) {
@@ -301,12 +299,10 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
       v[i] = make_uint4((uint32_t)u.x, (uint32_t)u.y, (uint32_t)u.z, (uint32_t)u.w);
     }
   };
-  // A workgroup takes blocks blockIdx.x, blockIdx.x + gridDim.x, ...: the
-  // next block's loads are issued as soon as the row tiles have used the
-  // registers, so they are in flight during the column phase.
-  int64_t blk = blockIdx.x;
-  if (blk < nblocks) load_block(blk);
-  for (; blk < nblocks; blk += gridDim.x) {
+  // A workgroup takes blocks blockIdx.x, blockIdx.x + gridDim.x, ... (one
+  // block each at the launch's grid; no registers held for a prefetch)
+  for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+    load_block(blk);
     const int64_t rb = blk / ncb;
     const int64_t kb = blk % ncb;
     const int64_t r0 = rb * 128, c0 = kb * 128;
@@ -338,7 +334,6 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
                                   reinterpret_cast<sv2i*>(q_row + (r0 + row) * ldq_row + c0 + l16 * 8));
       if (l16 == 0) s_row[kb * ld_s_row + r0 + row] = s;
     }
-    if (blk + gridDim.x < nblocks) load_block(blk + gridDim.x);
     __syncthreads();
 
     // ---- 128x1 column tiles, from LDS ----
@@ -547,7 +542,10 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int6
   const int64_t ncb = cols / 128;
   const int64_t nblocks = (rows / 128) * ncb;
   const int64_t nbr = rows / 128;
-  const int64_t grid = (nblocks + 1) / 2;      // two blocks per workgroup
+  // one block per workgroup: two per workgroup (the second prefetched during
+  // the first) measured 13% slower at X 4096x7168, whose 1792 blocks then
+  // filled fewer than one round of the 4 resident workgroups per CU
+  const int64_t grid = nblocks;
   if (tiled)
     hipLaunchKernelGGL(quant_dual_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, x, ldx, ncb,
                        nbr, nblocks, q_row, ldq_row, s_row, ld_s_row, q_col, ldq_col, s_col, ld_s_col);
@@ -563,7 +561,7 @@ hipError_t launch_quant_cols(const uint16_t* x, int64_t rows, int64_t cols, int6
   const int64_t ncb = (cols + 63) / 64;
   const int64_t nblocks = (rows / 128) * ncb;
   const int64_t nbr = rows / 128;
-  const int64_t grid = (nblocks + 1) / 2;      // two blocks per workgroup
+  const int64_t grid = nblocks;                // one block per workgroup (as the dual kernel)
   if (tiled)
     hipLaunchKernelGGL(quant_cols_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream,
                        x, cols, ldx, ncb, nbr, nblocks, q, ldq, scales, ld_s, amax_out);

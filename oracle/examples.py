@@ -7,8 +7,9 @@
 * ``per_tensor_vs_fine`` - "FP8 Mixed Precision: DeepSeek-V3 Training
   Architecture", Step 2: 64 tokens x 512 channels of 0.4 * N(0, 1) with +35
   added to channel 88, weights 1024 x 512 of 0.08 * N(0, 1) (legacy numpy
-  seed 42); relative Frobenius error of the GEMM with one scale per tensor
-  versus 1x128 / 128x128 scales.  Codes are on the E4M3 grid here (the page's
+  seed 42, kept as cited data); relative Frobenius error of the GEMM with one
+  scale per tensor versus 1x128 / 128x128 scales, computed with the oracle's
+  quantizers and block GEMM.  Codes are on the E4M3 grid here (the page's
   simulation rounds to integers instead).
 """
 from __future__ import annotations
@@ -52,21 +53,35 @@ def two_tiles(seed: int = 0):
 
 
 def per_tensor_vs_fine():
-    """Relative GEMM error, per-tensor vs fine-grained scales, on the E4M3 grid."""
+    """Relative GEMM error, per-tensor vs fine-grained scales, on the E4M3 grid.
+
+    The data are the page's fixture (its Step 2 values, kept as data): legacy
+    numpy seed 42, X = 0.4 N(0, 1) of 64 tokens x 512 channels with +35 on
+    channel 88, W = 0.08 N(0, 1) of 1024 x 512, both rounded to BF16 (the
+    method quantizes BF16 tensors).  Both quantizations and both GEMMs come
+    from the oracle's own functions: fine-grained = quant_rows (1x128) and
+    quant_weight (128x128) into gemm.fprop; per-tensor = the same codec with
+    one scale for the whole tensor (quant_rows_external with every tile's
+    scale equal), which the block GEMM applies exactly like a per-tensor
+    scale.  The reference is the float64 product of the BF16 inputs.
+    """
+    from . import gemm as og
     rs = np.random.RandomState(42)
     X = rs.randn(64, 512) * 0.4
     X[:, 88] += 35.0
     W = rs.randn(1024, 512) * 0.08
-    Y_ref = X @ W.T
-    X32, W32 = X.astype(np.float32), W.astype(np.float32)
-    Xt, _ = _groups_quant(X32.reshape(1, -1))
-    Wt, _ = _groups_quant(W32.reshape(1, -1))
-    Y_t = Xt.reshape(X.shape) @ Wt.reshape(W.shape).T
-    Xf, _ = _groups_quant(X32.reshape(64, 4, 128))
-    Wb = W32.reshape(8, 128, 4, 128).transpose(0, 2, 1, 3).reshape(8, 4, 128 * 128)
-    Wf, _ = _groups_quant(Wb)
-    Wf = Wf.reshape(8, 4, 128, 128).transpose(0, 2, 1, 3).reshape(1024, 512)
-    Y_f = Xf.reshape(X.shape) @ Wf.T
+    Xb, Wb = _f32_to_bf16(X.astype(np.float32)), _f32_to_bf16(W.astype(np.float32))
+    Y_ref = quant.bf16_to_f32(Xb).astype(np.float64) @ quant.bf16_to_f32(Wb).astype(np.float64).T
+    # fine-grained: 1x128 activation tiles, 128x128 weight blocks
+    Xq, sX = quant.quant_rows(Xb)
+    Wq, sW = quant.quant_weight(Wb)
+    Y_f = og.fprop(Xq, sX, Wq, sW)
+    # per-tensor: one scale from each tensor's max
+    sx = quant.scale_from_amax(np.max(np.abs(quant.bf16_to_f32(Xb))))
+    sw = quant.scale_from_amax(np.max(np.abs(quant.bf16_to_f32(Wb))))
+    Xq_t, _, _ = quant.quant_rows_external(Xb, np.full((64, 4), sx, np.float32))
+    Wq_t, _, _ = quant.quant_rows_external(Wb, np.full((1024, 4), sw, np.float32))
+    Y_t = og.fprop(Xq_t, np.full((64, 4), sx, np.float32), Wq_t, np.full((8, 4), sw, np.float32))
     err_t = np.linalg.norm(Y_t - Y_ref) / np.linalg.norm(Y_ref)
     err_f = np.linalg.norm(Y_f - Y_ref) / np.linalg.norm(Y_ref)
     return dict(err_per_tensor=float(err_t), err_fine=float(err_f))

@@ -146,9 +146,13 @@ __device__ __forceinline__ bool decode_tile_index(const GemmProblem& p, bool gro
       cum += ntm * tiles_n;
     }
     if (g >= p.groups) return false;
-    const int64_t local = b - cum;
-    m0 = lo + (local / tiles_n) * BM;
-    n0 = (local % tiles_n) * BN;
+    // within a group, the GroupM order of the plain layouts: a round of an
+    // XCD's workgroups covers 8 M tiles x fewer N tiles, so less of the
+    // expert's weights per round
+    int64_t tm, tn;
+    grouped_order(b - cum, ntm, tiles_n, tm, tn);
+    m0 = lo + tm * BM;
+    n0 = tn * BN;
     m_end = hi;
     Bp += (int64_t)g * p.N * p.ldb;
     sBp += (int64_t)g * (p.N / 128) * (p.K / BK);

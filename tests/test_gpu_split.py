@@ -17,29 +17,18 @@ import torch
 import synthetic as syn
 from oracle import gemm as og
 from oracle import quant
+from split_rule import persistent_grid, split_rule
 from test_gpu_gemm import act_scales_dev, bf16_bits, dev, rows_one_per_tile, tiled_bytes
 from tolerance import check_gemm, truncation_bound
 
 pytestmark = pytest.mark.gpu
 
 
-def expected_split(tiles, k_blocks, cus):
-    """The schedule rule, stated on its own: the persistent grid is the CU
-    count rounded down to a multiple of 8 (one workgroup per tile when there
-    are fewer tiles); with `left` = tiles mod grid leftover tiles, each is cut
-    into the fewest pieces that reach the shortest piece length allowed by
-    min(grid // left, 16, rounds of 4 K blocks) pieces, if that is >= 2."""
-    grid = cus // 8 * 8 if tiles > cus else tiles
-    rounds = (k_blocks + 3) // 4
-    if tiles <= grid or tiles % grid == 0:
-        return 0, 1
-    left = tiles % grid
-    most = min(grid // left, 16, rounds)
-    if most < 2:
-        return 0, 1
-    per = -(-rounds // most)
-    pieces = -(-rounds // per)
-    return (left, pieces) if pieces >= 2 else (0, 1)
+def expected_split(tiles, k_blocks, cus, slots=None):
+    """The schedule rule of tests/split_rule.py on this device: the
+    persistent grid from the CU count, the per-stream workspace of one
+    partial tile per CU."""
+    return split_rule(tiles, persistent_grid(tiles, cus), k_blocks, cus if slots is None else slots)
 
 
 def device_cus():

@@ -398,6 +398,34 @@ def test_division_shortcut_exhaustive(tmp_path):
     assert "scales=32640 scale_mismatches=0" in res.stdout
 
 
+def test_split_schedule_rule(tmp_path):
+    """split_plan / split_range (kernels.hpp) built on the host: every plan of
+    a grid of launches equals the rule stated in tests/split_rule.py, and the
+    program's invariant checks (pieces tile [0, K) in order, boundaries on
+    whole 4-block rounds, the pieces fit grid and workspace) all hold."""
+    from split_rule import split_rule
+    gxx = shutil.which("g++")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    if not gxx or not os.path.exists(os.path.join(rocm, "include", "hip", "hip_runtime.h")):
+        pytest.skip("g++ or the HIP headers are not available")
+    exe = str(tmp_path / "check_split_plan")
+    csrc = os.path.join(ROOT, "fine_grained_fp8_amd", "csrc")
+    r = subprocess.run([gxx, "-std=c++17", "-O1", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+                        "-I", csrc, os.path.join(ROOT, "tests", "c", "check_split_plan.cpp"), "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    lines = res.stdout.strip().splitlines()
+    assert res.returncode == 0 and lines[-1].endswith("violations=0"), lines[-1]
+    splits = 0
+    for ln in lines[:-1]:
+        tiles, grid, kb, slots, dp, st, pieces, rounds = map(int, ln.split())
+        assert (st, pieces) == split_rule(tiles, grid, kb, slots), ln
+        assert dp == tiles - st and rounds == (kb + 3) // 4, ln
+        splits += pieces > 1
+    assert splits > 100          # the grid exercises the split in many shapes
+
+
 def test_validation_layer_under_asan_ubsan(tmp_path):
     """The C-ABI layer (api.cpp: argument checks, range and alias
     arithmetic, device query) built on the host with g++

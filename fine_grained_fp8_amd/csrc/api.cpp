@@ -476,6 +476,8 @@ fp8_status block_gemm_impl(fp8_gemm_layout layout, int64_t M, int64_t N, int64_t
   fp8_status st = validate_gemm_common(M, N, K, A, lda, sA, ld_sa, B, sB, C, c_dtype, ldc);
   if (st != FP8_OK || M == 0) return st;
   if (layout != FP8_LAYOUT_WGRAD && N % 128 != 0) return FP8_ERR_SHAPE;
+  // the kernels number output tiles in 32 bits
+  if (((M + 127) / 128) * ((N + 255) / 256) >= (int64_t{1} << 31)) return FP8_ERR_UNSUPPORTED;
   int64_t b_rows, b_cols, sb_rows, sb_cols;
   switch (layout) {
     case FP8_LAYOUT_FPROP: b_rows = N; b_cols = K; sb_rows = N / 128; sb_cols = K / 128; break;
@@ -582,6 +584,8 @@ fp8_status grouped_impl(int32_t groups, const int32_t* offsets_dev, int64_t tota
   fp8_status st = validate_gemm_common(total_M, N, K, A, lda, sA, ld_sa, B, sB, C, c_dtype, ldc);
   if (st != FP8_OK || total_M == 0) return st;
   if (!offsets_dev) return FP8_ERR_NULL;
+  // tile count bound (every group may end in a ragged tile), numbered in 32 bits
+  if (((total_M + 127) / 128 + groups) * ((N + 255) / 256) >= (int64_t{1} << 31)) return FP8_ERR_UNSUPPORTED;
   if (!aligned4(offsets_dev)) return FP8_ERR_ALIGN;
   if (N % 128 != 0) return FP8_ERR_SHAPE;
   if (ldb < K || (tiled && ldb != K)) return FP8_ERR_LD;

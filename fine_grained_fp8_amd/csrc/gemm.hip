@@ -60,7 +60,8 @@ constexpr int kThreads = 256;
 constexpr int kWTile = BN * BK;   // 32 KB
 constexpr int kXTile = BM * BK;   // 16 KB
 constexpr int kScaleBytes = 2048; // token scales [256] + weight-side scales [256]
-constexpr int kGroupM = 8;
+constexpr int kGroupM = 8;   // a power of two
+static_assert((kGroupM & (kGroupM - 1)) == 0, "GroupM order masks with kGroupM - 1");
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 
 // Wave tile: 128 output columns (n) x 64 output rows (m); waves 2 (n) x 2 (m).
@@ -76,16 +77,25 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t total) {
   return (b & 7) * (total >> 3) + (b >> 3);
 }
 
-__device__ __forceinline__ void grouped_order(int64_t t, int64_t tiles_m, int64_t tiles_n,
+// GroupM order: tile t of a tiles_m x tiles_n grid walks groups of kGroupM
+// M tiles, column by column.  32-bit arithmetic (the host keeps tile counts
+// below 2^31): each 64-bit division by a runtime value is a long software
+// sequence, and this runs at every tile boundary.
+__device__ __forceinline__ void grouped_order(int64_t t64, int64_t tiles_m64, int64_t tiles_n64,
                                               int64_t& tm, int64_t& tn) {
-  const int64_t width = (int64_t)kGroupM * tiles_n;
-  const int64_t grp = t / width;
-  const int64_t first = grp * kGroupM;
-  int64_t gsz = tiles_m - first;
-  if (gsz > kGroupM) gsz = kGroupM;
-  const int64_t r = t - grp * width;
-  tm = first + r % gsz;
-  tn = r / gsz;
+  const uint32_t t = (uint32_t)t64, tiles_m = (uint32_t)tiles_m64, tiles_n = (uint32_t)tiles_n64;
+  const uint32_t width = (uint32_t)kGroupM * tiles_n;
+  const uint32_t grp = t / width;
+  const uint32_t first = grp * (uint32_t)kGroupM;
+  const uint32_t r = t - grp * width;
+  const uint32_t gsz = tiles_m - first < (uint32_t)kGroupM ? tiles_m - first : (uint32_t)kGroupM;
+  if (gsz == (uint32_t)kGroupM) {   // every group but a ragged last one
+    tm = first + (r & (kGroupM - 1));
+    tn = r / (uint32_t)kGroupM;
+  } else {
+    tm = first + r % gsz;
+    tn = r / gsz;
+  }
 }
 
 __device__ __forceinline__ v8i join(const v4i& lo, const v4i& hi) {
@@ -164,6 +174,60 @@ __device__ __forceinline__ bool decode_tile_index(const GemmProblem& p, bool gro
     n0 = tn * BN;
     m_end = p.M;
   }
+  return true;
+}
+
+// Grouped launches with at most kLdsGroups groups keep each group's clamped
+// row range and first tile index in LDS, built once per workgroup; the tile
+// decode then finds a tile's group with one compare per lane and a ballot
+// instead of a loop of dependent reads of the offsets in global memory.
+constexpr int kLdsGroups = 64;
+struct GroupLds {
+  int32_t* cum;   // [groups + 1]: tiles before group g
+  int32_t* lo;    // [groups]: clamped first row
+  int32_t* hi;    // [groups]: clamped end row
+};
+
+// Fill the table (wave 0; the caller's barrier publishes it).  Same clamping
+// as decode_tile_index.
+__device__ __forceinline__ void build_group_lds(const GemmProblem& p, const GroupLds& t, int lane) {
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  int32_t cnt = 0;
+  if (lane < p.groups) {
+    const int64_t lo = min(max((int64_t)p.offsets[lane], (int64_t)0), p.M);
+    const int64_t hi = min(max((int64_t)p.offsets[lane + 1], lo), p.M);
+    t.lo[lane] = (int32_t)lo;
+    t.hi[lane] = (int32_t)hi;
+    cnt = (int32_t)((hi - lo + BM - 1) / BM * tiles_n);
+  }
+  int32_t incl = cnt;   // inclusive scan over the wave's lanes
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane < p.groups) t.cum[lane + 1] = incl;
+  if (lane == 0) t.cum[0] = 0;
+}
+
+// decode_tile_index for a grouped launch through the LDS table.
+__device__ __forceinline__ bool decode_tile_lds(const GemmProblem& p, const GroupLds& t, int lane, int64_t b,
+                                                int64_t& m0, int64_t& m_end, int64_t& n0,
+                                                const uint8_t*& Bp, const float*& sBp) {
+  const int64_t tiles_n = (p.N + BN - 1) / BN;
+  bool hit = false;
+  if (lane < p.groups) hit = t.cum[lane] <= b && b < t.cum[lane + 1];   // empty groups never hit
+  const uint64_t mask = __ballot(hit);
+  if (mask == 0) return false;
+  const int g = __builtin_amdgcn_readfirstlane(__builtin_ctzll(mask));
+  const int64_t lo = t.lo[g], hi = t.hi[g];
+  int64_t tm, tn;
+  grouped_order(b - t.cum[g], (hi - lo + BM - 1) / BM, tiles_n, tm, tn);
+  m0 = lo + tm * BM;
+  n0 = tn * BN;
+  m_end = hi;
+  Bp = p.B + (int64_t)g * p.N * p.ldb;
+  sBp = p.sB + (int64_t)g * (p.N / 128) * (p.K / BK);
   return true;
 }
 
@@ -597,8 +661,21 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   };
   static_assert(4 * sizeof(PlanLds) <= kDWScaleOff - kDFreeOff, "schedule fits the free scale bytes");
   PlanLds* plan_lds = reinterpret_cast<PlanLds*>(lds_c2 + kDFreeOff) + wave;
+  // grouped launches of up to kLdsGroups groups: the group table in the free
+  // scale bytes of stages 1 (first tiles) and 3 (row ranges), which no DMA
+  // writes
+  static_assert((kLdsGroups + 1) * 4 <= kDWScaleOff - kDFreeOff && 2 * kLdsGroups * 4 <= kDWScaleOff - kDFreeOff,
+                "group table fits the free scale bytes");
+  const GroupLds gtab{reinterpret_cast<int32_t*>(lds_c1 + kDFreeOff), reinterpret_cast<int32_t*>(lds_c3 + kDFreeOff),
+                      reinterpret_cast<int32_t*>(lds_c3 + kDFreeOff) + kLdsGroups};
+  const bool group_lds = kGrouped && p.groups <= kLdsGroups;
+  if (group_lds) {
+    if (wave == 0) build_group_lds(p, gtab, lane);
+    __syncthreads();
+  }
   {
-    const int64_t n_tiles = kGrouped ? uniform_i64(grouped_tile_count(p)) : total_tiles;
+    const int64_t n_tiles =
+        kGrouped ? (group_lds ? (int64_t)gtab.cum[p.groups] : uniform_i64(grouped_tile_count(p))) : total_tiles;
     const SplitPlan pl = split_plan(n_tiles, gridDim.x, KB, p.ws_partial != nullptr ? p.ws_slots : 0);
     if (lane == 0)
       *plan_lds = PlanLds{pl.dp_tiles, pl.split_tiles, pl.dp_tiles + pl.split_tiles * pl.split, pl.split, pl.rounds};
@@ -624,6 +701,14 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   uint32_t sw_off = 0;
   const float* sa_tile = p.sA;      // token-side scales of the tile's rows, block 0
   const float* sb_tile = p.sB;      // Wgrad: weight-side scales of the tile's columns, block 0
+  // the same for the workgroup's next work item, decoded while the current
+  // one runs so that its last round can stream the next tile's first blocks
+  int nx_kb_lo = 0, nx_kb_hi = KB, nx_piece = -1, nx_rows_m = 0, nx_rows_n = 0;
+  int64_t nx_m0 = 0, nx_m_end = 0, nx_n0 = 0;
+  __amdgpu_buffer_rsrc_t nx_rsrc_x, nx_rsrc_w, nx_rsrc_sw;
+  uint32_t nx_sw_off = 0;
+  const float* nx_sa = p.sA;
+  const float* nx_sb = p.sB;
   const uint32_t sa_kbytes = (uint32_t)p.ld_sa * 4u, sb_kbytes = (uint32_t)p.ld_sb * 4u;
   // token-side tile: rows m0.., DMA'd 8 rows x 128 B per instruction, 16-byte
   // chunks XOR-swizzled by row & 7 (row & 7 == (lane >> 3) & 7 here)
@@ -649,17 +734,17 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   const int64_t sw_elems = kLayout == kFprop ? (p.N / 128) * p.ld_sb
                                              : (kLayout == kDgradT ? (p.K / BK) * p.ld_sb : 0);
   const uint32_t sw_kstride = kLayout == kFprop ? 4u : (uint32_t)p.ld_sb * 4u;
-  // decode work id `id` and set up its buffer resources; false if it names
-  // no tile
+  // decode work id `id` into the next-tile state and set up its buffer
+  // resources; false if it names no tile
   auto setup_tile = [&](int64_t id) -> bool {
     int64_t work_ids;
     const SplitPlan plan = load_plan(work_ids);
     int64_t b;
     if (id < plan.dp_tiles) {
       b = xcd_remap(id, plan.dp_tiles);
-      kb_lo = 0;
-      kb_hi = KB;
-      piece_slot = -1;
+      nx_kb_lo = 0;
+      nx_kb_hi = KB;
+      nx_piece = -1;
     } else {
       // pieces in K-range-major order, each XCD a contiguous run of them: an
       // XCD's pieces share one K range and neighbouring tiles, so its L2
@@ -670,29 +755,49 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
       b = plan.dp_tiles + t;
       int lo, hi;
       split_range(plan, range, KB, lo, hi);
-      kb_lo = __builtin_amdgcn_readfirstlane(lo);
-      kb_hi = __builtin_amdgcn_readfirstlane(hi);
+      nx_kb_lo = __builtin_amdgcn_readfirstlane(lo);
+      nx_kb_hi = __builtin_amdgcn_readfirstlane(hi);
       // the tile's partials lie together, in piece order
-      piece_slot = __builtin_amdgcn_readfirstlane(t * plan.split + range);
+      nx_piece = __builtin_amdgcn_readfirstlane(t * plan.split + range);
     }
-    if (!decode_tile_index(p, kGrouped, b, m0, m_end, n0, Bp, sBp)) return false;
-    m0 = uniform_i64(m0);
-    m_end = uniform_i64(m_end);
-    n0 = uniform_i64(n0);
+    int64_t tm0, tm_end, tn0;
+    if (group_lds ? !decode_tile_lds(p, gtab, lane, b, tm0, tm_end, tn0, Bp, sBp)
+                  : !decode_tile_index(p, kGrouped, b, tm0, tm_end, tn0, Bp, sBp))
+      return false;
+    nx_m0 = uniform_i64(tm0);
+    nx_m_end = uniform_i64(tm_end);
+    nx_n0 = uniform_i64(tn0);
     Bp = uniform_ptr(Bp);
     sBp = uniform_ptr(sBp);
-    rows_m = (int)(m_end - m0 < BM ? m_end - m0 : BM);
-    rows_n = (int)(p.N - n0 < BN ? p.N - n0 : BN);
-    rsrc_x = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + m0 * p.lda), (short)0, rows_m * (int)p.lda,
-                                               (int)kRsrcWord3);
-    rsrc_w = __builtin_amdgcn_make_buffer_rsrc((void*)(Bp + n0 * p.ldb), (short)0, rows_n * (int)p.ldb,
-                                               (int)kRsrcWord3);
-    rsrc_sw = __builtin_amdgcn_make_buffer_rsrc((void*)sBp, (short)0, (int)(sw_elems * 4), (int)kRsrcWord3);
-    const int64_t nbw = (n0 + 64 * wave) / 128;
-    sw_off = kLayout == kFprop ? (uint32_t)(nbw * p.ld_sb) * 4u : (uint32_t)nbw * 4u;
-    sa_tile = p.sA + m0;
-    sb_tile = sBp + n0;
+    nx_rows_m = (int)(nx_m_end - nx_m0 < BM ? nx_m_end - nx_m0 : BM);
+    nx_rows_n = (int)(p.N - nx_n0 < BN ? p.N - nx_n0 : BN);
+    nx_rsrc_x = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + nx_m0 * p.lda), (short)0, nx_rows_m * (int)p.lda,
+                                                  (int)kRsrcWord3);
+    nx_rsrc_w = __builtin_amdgcn_make_buffer_rsrc((void*)(Bp + nx_n0 * p.ldb), (short)0, nx_rows_n * (int)p.ldb,
+                                                  (int)kRsrcWord3);
+    nx_rsrc_sw = __builtin_amdgcn_make_buffer_rsrc((void*)sBp, (short)0, (int)(sw_elems * 4), (int)kRsrcWord3);
+    const int64_t nbw = (nx_n0 + 64 * wave) / 128;
+    nx_sw_off = kLayout == kFprop ? (uint32_t)(nbw * p.ld_sb) * 4u : (uint32_t)nbw * 4u;
+    nx_sa = p.sA + nx_m0;
+    nx_sb = sBp + nx_n0;
     return true;
+  };
+  // the next-tile state becomes the current one
+  auto adopt_next = [&]() {
+    kb_lo = nx_kb_lo;
+    kb_hi = nx_kb_hi;
+    piece_slot = nx_piece;
+    m0 = nx_m0;
+    m_end = nx_m_end;
+    n0 = nx_n0;
+    rows_m = nx_rows_m;
+    rows_n = nx_rows_n;
+    rsrc_x = nx_rsrc_x;
+    rsrc_w = nx_rsrc_w;
+    rsrc_sw = nx_rsrc_sw;
+    sw_off = nx_sw_off;
+    sa_tile = nx_sa;
+    sb_tile = nx_sb;
   };
   int64_t tile = blockIdx.x;
   {
@@ -700,11 +805,31 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     (void)load_plan(work_ids);
     while (tile < work_ids && !setup_tile(tile)) tile += gridDim.x;
     if (tile >= work_ids) return;
+    adopt_next();
   }
 
-  auto issue_load = [&](int kb, int op, auto stage, v8i (&wr)[DNI]) {
+  auto this_rsrc_x = [&]() { return rsrc_x; };
+  auto this_rsrc_w = [&]() { return rsrc_w; };
+  auto this_rsrc_sw = [&]() { return rsrc_sw; };
+  auto this_sw_off = [&]() { return sw_off; };
+  auto this_sa = [&]() { return sa_tile; };
+  auto this_sb = [&]() { return sb_tile; };
+  auto this_rows_m = [&]() { return rows_m; };
+  auto this_rows_n = [&]() { return rows_n; };
+  // kNext: the load belongs to the next work item (its first blocks, streamed
+  // by the current tile's last round)
+  auto issue_load = [&](int kb, int op, auto stage, v8i (&wr)[DNI], auto next_tag) {
+    constexpr bool kNext = decltype(next_tag)::value;
     lds_u8* st = tile_lds(stage);
     lds_u8* sc = scl_lds(stage);
+    const __amdgpu_buffer_rsrc_t rsrc_x = kNext ? nx_rsrc_x : this_rsrc_x();
+    const __amdgpu_buffer_rsrc_t rsrc_w = kNext ? nx_rsrc_w : this_rsrc_w();
+    const __amdgpu_buffer_rsrc_t rsrc_sw = kNext ? nx_rsrc_sw : this_rsrc_sw();
+    const uint32_t sw_off = kNext ? nx_sw_off : this_sw_off();
+    const float* sa_tile = kNext ? nx_sa : this_sa();
+    const float* sb_tile = kNext ? nx_sb : this_sb();
+    const int rows_m = kNext ? nx_rows_m : this_rows_m();
+    const int rows_n = kNext ? nx_rows_n : this_rows_n();
     // the per-step part of an address in the vector offset (one add per step,
     // shared by the step's loads), the per-load constant in the scalar offset;
     // the range check sees their sum, as before
@@ -803,8 +928,17 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     bxb = pair(stn + x_lo + 2048, stn + x_hi + 2048);
   };
 
+  auto nx_clamp = [&](int b) { return b < nx_kb_hi ? b : nx_kb_hi - 1; };
+  using cur_t = std::integral_constant<bool, false>;
+  using nxt_t = std::integral_constant<bool, true>;
+  // xj_tag: -1 in every round but a tile's last; there, the step's index j in
+  // the tile's last round, whose loads past the tile's last block fetch the
+  // next work item's first blocks instead (its DMA from step 2 on, its
+  // weights from step 1 on) - the blocks its prologue would load, into the
+  // same stages and registers
   auto step = [&](auto pad_tag, int kb, auto s_cur, v8i (&wc)[DNI], auto s_next, auto s_dma,
-                  v8i (&wf)[DNI]) {
+                  v8i (&wf)[DNI], auto xj_tag) {
+    constexpr int XJ = decltype(xj_tag)::value;
     const uint8_t* st = tile_of(s_cur);
     const uint8_t* sc = scl_of(s_cur);
     const uint8_t* stn = tile_of(s_next);
@@ -874,7 +1008,15 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
         }
         if ((i & 1) && 2 * j + (i >> 1) < kDOpsPerBlock) {
           const int op = 2 * j + (i >> 1);
-          issue_load(op < kDDmaOps ? kb_d : kb_w, op, s_dma, wf);
+          if constexpr (XJ < 0) {
+            issue_load(op < kDDmaOps ? kb_d : kb_w, op, s_dma, wf, cur_t{});
+          } else if (op < kDDmaOps) {
+            if constexpr (XJ >= 2) issue_load(nx_clamp(nx_kb_lo + XJ - 2), op, s_dma, wf, nxt_t{});
+            else issue_load(kb_d, op, s_dma, wf, cur_t{});
+          } else {
+            if constexpr (XJ >= 1) issue_load(nx_clamp(nx_kb_lo + XJ - 1), op, s_dma, wf, nxt_t{});
+            else issue_load(kb_w, op, s_dma, wf, cur_t{});
+          }
         }
         if (j == DNJ - 2) {
           if (i == 0) an_l = *reinterpret_cast<const v4i*>(stn + x_lo);
@@ -927,15 +1069,15 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   auto issue_prologue = [&]() {
     auto clamp = [&](int b) { return b < kb_hi ? b : kb_hi - 1; };
 #pragma unroll
-    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(kb_lo, op, S0{}, w0);
+    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(kb_lo, op, S0{}, w0, cur_t{});
 #pragma unroll
-    for (int op = 0; op < kDDmaOps; ++op) issue_load(kb_lo, op, S0{}, w0);
+    for (int op = 0; op < kDDmaOps; ++op) issue_load(kb_lo, op, S0{}, w0, cur_t{});
 #pragma unroll
-    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(kb_lo + 1), op, S1{}, w1);
+    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(kb_lo + 1), op, S1{}, w1, cur_t{});
 #pragma unroll
-    for (int op = 0; op < kDDmaOps; ++op) issue_load(clamp(kb_lo + 1), op, S1{}, w1);
+    for (int op = 0; op < kDDmaOps; ++op) issue_load(clamp(kb_lo + 1), op, S1{}, w1, cur_t{});
 #pragma unroll
-    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(kb_lo + 2), op, S2{}, w2);
+    for (int op = kDDmaOps; op < kDOpsPerBlock; ++op) issue_load(clamp(kb_lo + 2), op, S2{}, w2, cur_t{});
   };
   // ---- epilogue: lane holds 4 consecutive n of row m for every (i, j) ----
   auto store_tile = [&](int64_t em0, int64_t em_end, int64_t en0, int erows_m, int erows_n) {
@@ -1007,49 +1149,65 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   };
   zero_state();
   issue_prologue();
+  // Each work item decodes the next one first.  Its last round (padded
+  // with scale-0 steps when the item's K blocks are not a multiple of four)
+  // streams the next item's first blocks into the stages and registers the
+  // prologue would use, so the item's stores overlap those loads and the
+  // next item starts without a prologue.  A workgroup's last item streams
+  // its own last block again instead (harmless reloads, drained at the end).
   for (;;) {
   wait_vm<kDDmaOps + 2 * kDWOps>();
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
+  int64_t next = tile + gridDim.x;
+  bool more;
+  {
+    int64_t work_ids;
+    (void)load_plan(work_ids);
+    while (next < work_ids && !setup_tile(next)) next += gridDim.x;
+    more = next < work_ids;
+  }
+  if (!more) {
+    // no next item: its "first blocks" are this tile's last block
+    nx_kb_lo = kb_hi - 1;
+    nx_kb_hi = kb_hi;
+    nx_rows_m = rows_m;
+    nx_rows_n = rows_n;
+    nx_rsrc_x = rsrc_x;
+    nx_rsrc_w = rsrc_w;
+    nx_rsrc_sw = rsrc_sw;
+    nx_sw_off = sw_off;
+    nx_sa = sa_tile;
+    nx_sb = sb_tile;
+  }
   prefetch(S0{});
   using no_pad = std::integral_constant<bool, false>;
   using pad = std::integral_constant<bool, true>;
-  const int kb_end4 = kb_lo + ((kb_hi - kb_lo) & ~3);
+  using xn = std::integral_constant<int, -1>;
+  const int kb_last = kb_lo + ((kb_hi - kb_lo + 3) & ~3) - 4;   // first block of the last round
   int kb = kb_lo;
-  for (; kb < kb_end4; kb += 4) {
-    step(no_pad{}, kb, S0{}, w0, S1{}, S2{}, w3);
-    step(no_pad{}, kb + 1, S1{}, w1, S2{}, S3{}, w0);
-    step(no_pad{}, kb + 2, S2{}, w2, S3{}, S0{}, w1);
-    step(no_pad{}, kb + 3, S3{}, w3, S0{}, S1{}, w2);
+  for (; kb < kb_last; kb += 4) {
+    step(no_pad{}, kb, S0{}, w0, S1{}, S2{}, w3, xn{});
+    step(no_pad{}, kb + 1, S1{}, w1, S2{}, S3{}, w0, xn{});
+    step(no_pad{}, kb + 2, S2{}, w2, S3{}, S0{}, w1, xn{});
+    step(no_pad{}, kb + 3, S3{}, w3, S0{}, S1{}, w2, xn{});
   }
-  if (kb < kb_hi) {
-    step(pad{}, kb, S0{}, w0, S1{}, S2{}, w3);
-    step(pad{}, kb + 1, S1{}, w1, S2{}, S3{}, w0);
-    step(pad{}, kb + 2, S2{}, w2, S3{}, S0{}, w1);
-    step(pad{}, kb + 3, S3{}, w3, S0{}, S1{}, w2);
-  }
+  step(pad{}, kb, S0{}, w0, S1{}, S2{}, w3, std::integral_constant<int, 0>{});
+  step(pad{}, kb + 1, S1{}, w1, S2{}, S3{}, w0, std::integral_constant<int, 1>{});
+  step(pad{}, kb + 2, S2{}, w2, S3{}, S0{}, w1, std::integral_constant<int, 2>{});
+  step(pad{}, kb + 3, S3{}, w3, S0{}, S1{}, w2, std::integral_constant<int, 3>{});
   if constexpr (kBlockW) {
 #pragma unroll
     for (int i = 0; i < DNI; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[i][DNJ - 1][v] = __builtin_fmaf(Pl[i][v], cl, acc[i][DNJ - 1][v]);
   }
-  // the last steps' reload DMA has landed and every wave is done with the
-  // stages before the next tile's DMA reuses them
-  wait_vm_lgkm0<0>();
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
   const int64_t em0 = m0, em_end = m_end, en0 = n0;
   const int erows_m = rows_m, erows_n = rows_n;
   const int epiece = piece_slot;
-  int64_t next = tile + gridDim.x;
   int64_t work_ids;
   const SplitPlan plan = load_plan(work_ids);
-  while (next < work_ids && !setup_tile(next)) next += gridDim.x;
-  const bool more = next < work_ids;
-  if (more) issue_prologue();
   if (epiece >= 0) {
     // A K piece of a split tile (a workgroup's last work item).  Its FP32
     // partial tile goes to the workspace in fragment order (16 B per lane per
@@ -1123,7 +1281,11 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     return;
   }
   store_tile(em0, em_end, en0, erows_m, erows_n);
-  if (!more) break;
+  if (!more) {
+    wait_vm<0>();   // the reloads streamed by the last round land before the workgroup ends
+    break;
+  }
+  adopt_next();
   tile = next;
   zero_state();
   }

@@ -298,6 +298,35 @@ def test_grouped_small_with_empty_and_tiny_groups(gpu_lib):
     check_gemm(bf16_bits(C), R, T, 384, E=E, label="grouped small")
 
 
+@pytest.mark.parametrize("groups", [64, 80])
+def test_grouped_many_groups(gpu_lib, groups):
+    """Up to 64 groups the persistent kernel decodes tiles through a copy of
+    the group table in LDS, beyond that through the offsets in device memory:
+    64 and 80 groups (empty, one-row and multi-tile groups, K 256, N 256)
+    against the oracle, row-major and operand-tiled weights bit-identical."""
+    rng = np.random.default_rng(900 + groups)
+    counts = rng.integers(0, 300, size=groups)
+    counts[::7] = 0
+    counts[3] = 1
+    off = syn.expert_offsets(counts)
+    K, N = 256, 256
+    xb = syn.activation_with_outliers(int(counts.sum()), K, seed=71)
+    Xq, sX = quant.quant_rows(xb)
+    ws = [quant.quant_weight(syn.gaussian((N, K), seed=2000 + e, std=0.02)) for e in range(groups)]
+    Wq_e, sW_e = [w[0] for w in ws], [w[1] for w in ws]
+    R, T = og.grouped_fprop(Xq, sX, off, Wq_e, sW_e, with_magnitude=True)
+    E = np.concatenate([truncation_bound(Xq[off[e]:off[e + 1]], sX[off[e]:off[e + 1]], Wq_e[e],
+                                         og.expand_block_scales(sW_e[e], N)) for e in range(groups)])
+    C = run_grouped(gpu_lib, Xq, sX, off, Wq_e, sW_e)
+    offd = dev(off.astype(np.int32))
+    Ct = gpu_lib.block_gemm_grouped(offd, dev(Xq), act_scales_dev(sX),
+                                    dev(np.stack([tiled_bytes(w) for w in Wq_e])), dev(np.stack(sW_e)),
+                                    tiled=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), Ct.view(torch.int16)), "tiled and row-major differ"
+    check_gemm(bf16_bits(C), R, T, K, E=E, label=f"grouped {groups} groups")
+
+
 def test_grouped_full_size_sampled(gpu_lib):
     """Config 5 as the bench times it (8 experts, 16384 tokens split by a
     seeded multinomial, N 2048, K 7168, operand-tiled expert weights): one row

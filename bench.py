@@ -32,8 +32,12 @@ seeded synthetic inputs already resident in HBM:
              kernel that calibrates the HBM byte counters
 
 `value` is the metric's headline: TFLOP/s of the fprop row including its
-quantization (2*M*N*K / (t_quant + t_gemm)), from HIP events on the launch
-stream averaged over the timed steps.  Other rows are reported under "rows".
+quantization, 2*M*N*K / t_region, where t_region is the back-to-back
+quantize-then-GEMM region, from HIP events on the launch stream averaged over
+the timed steps.  Other rows are reported under "rows".  Beside the dual
+(both-orientation) quantizers the bench times torch's copy of the same BF16
+tensor, which moves the same bytes (read 2, write 2 per value): the rate a
+plain kernel reaches on that traffic mix at that size.
 
     python bench.py [--steps K (50)] [--warmup W (10)] [--gpus 1] [--no-cpu-baseline]
 """
@@ -301,6 +305,8 @@ def main():
         d["msg6"] = fp8.pack_tokens(d["x3"], d["src6"])
     if want("backward"):
         d["dy4"] = to_dev(syn.gaussian((4096, 18432), seed=4, std=1e-3), torch)
+        d["dy4_copy"] = torch.empty_like(d["dy4"])
+        d["x3_copy"] = torch.empty_like(d["x3"])
     if want("grouped"):
         counts = syn.expert_counts(16384, 8, seed=0)
         d["off5"] = to_dev(syn.expert_offsets(counts).astype(np.int32), torch)
@@ -367,6 +373,9 @@ def main():
             # X in both orientations from one read (Fprop rows, saved columns for Wgrad)
             tm.region("fwd.quant_dual_x", lambda: fp8.quant_act_dual(d["x3"], tiled=True))
             tm.region("fwd.quant_row_x", lambda: fp8.quant_act_1x128(d["x3"], "row"))
+            # torch's copy kernel on the dual passes' read/write bytes
+            tm.region("ref.copy_dy", lambda: d["dy4_copy"].copy_(d["dy4"]))
+            tm.region("ref.copy_x", lambda: d["x3_copy"].copy_(d["x3"]))
         if want("grouped"):
             (q, s, _), _ = tm.chain("grouped", [
                 ("grouped.quant", lambda: fp8.quant_act_1x128(d["x5"], "row")),
@@ -528,15 +537,19 @@ def main():
         tq3, tg2 = tm.mean_ms("wgrad.quant_x"), tm.mean_ms("wgrad.gemm")
         trow, tcol = tm.mean_ms("bwd.quant_row"), tm.mean_ms("bwd.quant_col")
         EL = 4096 * 18432
+        tcd = tm.mean_ms("ref.copy_dy")
         rows["dual_quant"] = {"ms": tdual, "GB/s": EL * (2 + 2 + 8 / 128) / tdual / 1e6,
                               "ms_separate_row_plus_col": trow + tcol,
                               "GB/s_separate": EL * 2 * (3 + 4 / 128) / (trow + tcol) / 1e6,
-                              "speedup_vs_separate": (trow + tcol) / tdual}
+                              "speedup_vs_separate": (trow + tcol) / tdual,
+                              "ms_same_traffic_copy": tcd, "frac_of_same_traffic_copy": tcd / tdual}
         tdx = tm.mean_ms("fwd.quant_dual_x")
         tsx = tm.mean_ms("fwd.quant_row_x") + tm.mean_ms("wgrad.quant_x")
         EX = 4096 * 7168
+        tcx = tm.mean_ms("ref.copy_x")
         rows["dual_quant_x"] = {"ms": tdx, "GB/s": EX * (2 + 2 + 8 / 128) / tdx / 1e6,
-                                "ms_separate_row_plus_col": tsx, "speedup_vs_separate": tsx / tdx}
+                                "ms_separate_row_plus_col": tsx, "speedup_vs_separate": tsx / tdx,
+                                "ms_same_traffic_copy": tcx, "frac_of_same_traffic_copy": tcx / tdx}
         # each GEMM is charged the share of the dual pass its operand costs
         tq1 = tq2 = tdual / 2
         tdr = tm.mean_ms("dgrad_rowmajor.gemm")

@@ -645,8 +645,9 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
   auto tile_lds = [&](auto k) -> lds_u8* { return (lds_u8*)tile_of(k); };
   auto scl_lds = [&](auto k) -> lds_u8* { return (lds_u8*)scl_of(k); };
 
-  // Persistent: the workgroup takes work ids blockIdx.x, + gridDim.x, ...
-  // and starts the loads of its next tile before it stores the current one.
+  // Persistent: the workgroup takes work ids blockIdx.x, + gridDim.x, ...;
+  // each tile's last round streams the next tile's first blocks, so the
+  // tile's stores overlap them.
   // Ids below plan.dp_tiles are whole tiles (gridDim.x is a multiple of 8,
   // so all of a workgroup's tiles lie in the same XCD's run); the ids after
   // them are the K pieces of the leftover tiles, one per workgroup, summed by
@@ -1058,14 +1059,16 @@ __global__ __launch_bounds__(kThreads, 1) void block_gemm_direct_kernel(GemmProb
     }
   };
 
-  // Prologue of a tile, in the steady-state order (weights of its first
-  // block; tile of the first block and weights of the second; tile of the
-  // second and weights of the third), blocks past the tile's K range
-  // repeating its last block.  Its wait allows the 22 loads
-  // issued after block 0's tile (any stores issued after them are younger
-  // still), then block 0's first operands are read.  Whole rounds of four
-  // steps follow with no conditions inside; when K is not a multiple of four
-  // blocks the last round pads with steps that fold with scale 0.
+  // Prologue of the workgroup's first tile, in the steady-state order
+  // (weights of its first block; tile of the first block and weights of the
+  // second; tile of the second and weights of the third), blocks past the
+  // tile's K range repeating its last block; later tiles get the same loads
+  // from the previous tile's last round.  The wait at the top of each tile
+  // allows the 22 loads issued after block 0's tile (any stores issued after
+  // them are younger still), then block 0's first operands are read.  Whole
+  // rounds of four steps follow with no conditions inside; when K is not a
+  // multiple of four blocks the last round pads with steps that fold with
+  // scale 0.
   auto issue_prologue = [&]() {
     auto clamp = [&](int b) { return b < kb_hi ? b : kb_hi - 1; };
 #pragma unroll

@@ -147,6 +147,12 @@ def test_gemm_validation(lib):
     # scale tables of 2 GiB or more are not addressable with 32-bit offsets
     assert gemm(lib, ld_sa=1 << 28) == UNSUP                  # 4 K blocks x 2^28 floats
     assert gemm(lib, layout=2, ld_sb=1 << 28, dt=1) == UNSUP
+    # the kernels number output tiles in 32 bits: 2^21 x 2^10 tiles is refused
+    # before any other check looks at the (fake) buffers
+    big_m, big_n = 1 << 28, 1 << 18
+    assert gemm(lib, M=big_m, N=big_n, K=128, lda=128, ld_sa=big_m, ldb=128, ld_sb=1, ldc=big_n) == UNSUP
+    assert gemm(lib, M=big_m, N=big_n - 256, K=128, lda=128, ld_sa=big_m, ldb=128, ld_sb=1,
+                ldc=big_n) != UNSUP                                # 2^31 - 2^21 tiles pass this check
 
 
 def fused(lib, M=256, N=256, K=512, x=X, ldx=512, w=B, ldw=512, sw=S2, ld_sw=4, c=C, dt=0, ldc=256,
@@ -370,6 +376,9 @@ def test_grouped_validation(lib):
     assert f(*bad) == SHAPE
     bad = list(args); bad[10] = 256
     assert f(*bad) == LD
+    # tile bound with one ragged tile per group: (2^21 + 8) x 2^10 >= 2^31
+    big = [8, X, 1 << 28, 1 << 18, 128, A, 128, S, 1 << 28, B, 128, S2, C, 0, 1 << 18, None]
+    assert f(*big) == UNSUP
 
 
 def test_no_device_reported_without_gpu(lib):

@@ -224,8 +224,9 @@ fp8_status fp8_quant_weight_128x128_tiled(const void* w, int64_t rows, int64_t c
  *     become whole contiguous lines.
  *  C: [M][ldc >= N], BF16 (round to nearest even) or FP32 (c_dtype).
  *  M == 0 is a no-op.  C must not overlap A, B or the scales.
- *  Limits (FP8_ERR_UNSUPPORTED beyond them): lda, ldb <= 2^23, and each
- *  scale table (its rows x ld x 4 bytes) under 2 GiB.
+ *  Limits (FP8_ERR_UNSUPPORTED beyond them): lda, ldb <= 2^23, each scale
+ *  table (its rows x ld x 4 bytes) under 2 GiB, and fewer than 2^31 output
+ *  tiles of 128 x 256 (grouped: counting one ragged tile per group).
  *  Workspace: FPROP, DGRAD_T and WGRAD run on a persistent grid of one
  *  workgroup per CU.  When the output tiles leave that grid's last round at
  *  most half full, the leftover tiles are cut along K and their FP32 partial
@@ -306,6 +307,7 @@ fp8_status fp8_block_gemm_fused_quant(int64_t M, int64_t N, int64_t K, const voi
  *  C   [total_M][ldc >= N], BF16 or FP32.   N % 128 == 0, K % 128 == 0.
  *  The tiles are counted on the device from the offsets; the split of
  *  leftover tiles and its per-stream workspace are as for fp8_block_gemm.
+ *  Limits as for fp8_block_gemm.
  */
 fp8_status fp8_block_gemm_grouped(int32_t groups, const int32_t* offsets_dev, int64_t total_M,
                                   int64_t N, int64_t K, const uint8_t* A, int64_t lda,

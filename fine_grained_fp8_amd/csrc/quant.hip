@@ -274,10 +274,12 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(
 // staged in LDS, where eight lanes share two adjacent columns (16 rows each)
 // and combine the column max with DPP.  Input and codes are streamed
 // (non-temporal).  Every code and scale equals the one the separate row and
-// column quantizers produce.
+// column quantizers produce.  The 32 KB tile admits four workgroups per CU
+// (measured: 31 KB would admit five), so the register bound is set for four:
+// at five the operand-tiled form spilled a register into scratch.
 // ---------------------------------------------------------------------------
 template <bool kTiled>
-__global__ __launch_bounds__(256, 5) void quant_dual_kernel(
+__global__ __launch_bounds__(256, 4) void quant_dual_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t ncb, int64_t nbr, int64_t nblocks,
     uint8_t* __restrict__ q_row, int64_t ldq_row, float* __restrict__ s_row, int64_t ld_s_row,
     uint8_t* __restrict__ q_col, int64_t ldq_col, float* __restrict__ s_col, int64_t ld_s_col) {

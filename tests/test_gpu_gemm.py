@@ -393,6 +393,71 @@ def test_grouped_malformed_offsets_stay_inside_the_rows(gpu_lib):
                        label=f"grouped clamp {off[:4]} tiled={tiled}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (5, 128, 256), (129, 128, 384)])
+def test_degenerate_shapes(gpu_lib, M, N, K):
+    """Edge shapes: a single token row; one 128-wide column block (half of a
+    256-wide output tile, the other half past N); one K block (a pipeline
+    round of four steps, three of them padding that folds with scale 0); a
+    row tile holding one valid row after a full one.  BF16 out against the
+    oracle; the operand-tiled weights bit-identical to the row-major ones."""
+    xb = syn.activation_with_outliers(M, K, seed=1000 + M)
+    wb = syn.gaussian((N, K), seed=2000 + N, std=0.02)
+    Xq, sX = quant.quant_rows(xb)
+    Wq, sW = quant.quant_weight(wb)
+    R, T = og.fprop(Xq, sX, Wq, sW, with_magnitude=True)
+    sWn = og.expand_block_scales(sW, N)
+    C = run_fprop(gpu_lib, Xq, sX, Wq, sW)
+    check_gemm(bf16_bits(C), R, T, K, label=f"degenerate {M}x{N}x{K}",
+               E_at=lambda r, c: truncation_bound_at(Xq, sX, Wq, sWn, r, c))
+    Ct = gpu_lib.block_gemm("fprop_tiled", dev(Xq), act_scales_dev(sX), dev(tiled_bytes(Wq)), dev(sW))
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), Ct.view(torch.int16))
+
+
+def test_single_row_against_full_weights(gpu_lib, big_layer):
+    """One token row (M = 1: one row tile with 127 rows past M) against the
+    full 18432x7168 weights, every output element against the oracle, and
+    equal to that row of the full 4096-row launch: a tile's rows do not
+    interact."""
+    Xq, sX, Wq, sW = big_layer
+    B, sB = dev(tiled_bytes(Wq)), dev(sW)
+    C1 = gpu_lib.block_gemm("fprop_tiled", dev(Xq[:1]), act_scales_dev(sX[:1]), B, sB)
+    C = gpu_lib.block_gemm("fprop_tiled", dev(Xq), act_scales_dev(sX), B, sB)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C[:1].view(torch.int16)), "row 0 alone differs from row 0 of the layer"
+    R, T = og.fprop(Xq[:1], sX[:1], Wq, sW, with_magnitude=True)
+    sWn = og.expand_block_scales(sW, 18432)
+    check_gemm(bf16_bits(C1), R, T, 7168, label="one row 1x18432x7168",
+               E_at=lambda r, c: truncation_bound_at(Xq[:1], sX[:1], Wq, sWn, r, c))
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_grouped_single_group_equals_fprop(gpu_lib, tiled):
+    """One group holding every row is a plain Fprop: the grouped launch must
+    equal fp8_block_gemm bit for bit (the same tiles in the same order, the
+    same split schedule).  4174 rows x N 2048 x K 1024 gives 264 tiles: more
+    than one per persistent workgroup, a ragged last row tile and a split
+    tail of 8 tiles; one row per M tile is also checked against the
+    oracle."""
+    M, N, K = 4174, 2048, 1024
+    xb = syn.activation_with_outliers(M, K, seed=91)
+    wb = syn.gaussian((N, K), seed=92, std=0.02)
+    Xq, sX = quant.quant_rows(xb)
+    Wq, sW = quant.quant_weight(wb)
+    A, sA = dev(Xq), act_scales_dev(sX)
+    B = dev(tiled_bytes(Wq)) if tiled else dev(Wq)
+    C = gpu_lib.block_gemm("fprop_tiled" if tiled else "fprop", A, sA, B, dev(sW))
+    off = dev(np.array([0, M], np.int32))
+    Cg = gpu_lib.block_gemm_grouped(off, A, sA, B.reshape(1, N, K).contiguous(), dev(sW[None]), tiled=tiled)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), Cg.view(torch.int16)), "grouped (one group) and plain Fprop differ"
+    rows = rows_one_per_tile(M, seed=93)
+    R, T = og.fprop(Xq[rows], sX[rows], Wq, sW, with_magnitude=True)
+    sWn = og.expand_block_scales(sW, N)
+    check_gemm(bf16_bits(Cg)[rows], R, T, K, label=f"grouped one group {M}x{N}x{K}",
+               E_at=lambda r, c: truncation_bound_at(Xq[rows], sX[rows], Wq, sWn, r, c))
+
+
 # ---------------------------------------------------------------------------
 # Operand-tiled weight codes: the quantizer's tiled bytes against the
 # oracle's layout, and every tiled GEMM bit-identical to its row-major twin.

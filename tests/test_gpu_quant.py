@@ -193,6 +193,24 @@ def test_quant_dual_small(gpu_lib, case):
     assert_dual_match(gpu_lib, x, label=case)
 
 
+@pytest.mark.parametrize("M,K", [(1, 128), (1, 7168), (3, 256), (130, 128)])
+def test_quant_rows_degenerate(gpu_lib, M, K):
+    """One and a few rows, one tile wide and a layer wide, and a row count
+    just past a multiple of 128: codes, scales and amax bit-exact."""
+    x = syn.activation_with_outliers(M, K, seed=500 + M + K)
+    assert_rows_match(gpu_lib, x, label=f"rows {M}x{K}")
+
+
+@pytest.mark.parametrize("M,C", [(128, 8), (128, 128), (128, 7168)])
+def test_quant_cols_and_dual_degenerate(gpu_lib, M, C):
+    """One 128-token block: eight columns (the narrowest 16-byte row), one
+    column block, and a layer wide; the dual pass where C is whole blocks."""
+    x = syn.gaussian((M, C), seed=600 + C, std=1e-3)
+    assert_cols_match(gpu_lib, x, label=f"cols {M}x{C}")
+    if C % 128 == 0:
+        assert_dual_match(gpu_lib, x, label=f"dual {M}x{C}")
+
+
 def test_quant_dual_full_size(gpu_lib):
     """dY 4096x18432: both orientations equal the separate passes everywhere
     (compared on the GPU) and the oracle on a sample of rows and columns."""

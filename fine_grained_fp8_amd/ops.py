@@ -47,7 +47,7 @@ _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 
 def quant_act_1x128(x: torch.Tensor, direction: str = "row", *, scales_in=None,
-                    return_amax: bool = False, sat_count=None, stream=None):
+                    return_amax: bool = False, sat_count=None, out=None, scales_out=None, stream=None):
     """Online FP8 quantization of activations.
 
     direction "row": 1x128 tiles along each row; returns
@@ -59,6 +59,9 @@ def quant_act_1x128(x: torch.Tensor, direction: str = "row", *, scales_in=None,
     scales_in (row only): caller scales in the scale layout; then the returned
     scales are None.  return_amax adds the per-tile max |x| (same layout).
     sat_count: optional int32/uint32 device tensor of one element, incremented.
+    out / scales_out: optional caller buffers for q (the shape above, uint8)
+    and the scales (at least the shape above, float32, row-major; its row
+    stride is passed as ld_s), so that repeated calls allocate nothing.
     Returns (q, scales, amax_or_None).
     """
     lib = _lib.load_library()
@@ -66,19 +69,32 @@ def quant_act_1x128(x: torch.Tensor, direction: str = "row", *, scales_in=None,
     rows, cols = x.shape
     dev = x.device
     if direction == "row":
-        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        q_shape = (rows, cols)
         s_shape = (cols // 128, round_up(rows, 4))
         tile_dir = _lib.TILE_ROW
     elif direction in ("col", "col_tiled"):
-        q = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+        q_shape = (cols, rows)
         s_shape = (rows // 128, round_up(cols, 4))
         tile_dir = _lib.TILE_COL if direction == "col" else _lib.TILE_COL_TILED
     else:
         raise ValueError(direction)
+    if out is None:
+        q = torch.empty(q_shape, dtype=torch.uint8, device=dev)
+    else:
+        _check_2d("out", out, (torch.uint8, torch.float8_e4m3fn))
+        if tuple(out.shape) != q_shape or not out.is_contiguous():
+            raise ValueError(f"out: expected a contiguous {q_shape} tensor, got {tuple(out.shape)}")
+        q = out
     if scales_in is not None:
         _check_2d("scales_in", scales_in, (torch.float32,))
         scales = None
         ld_s = scales_in.stride(0)
+    elif scales_out is not None:
+        _check_2d("scales_out", scales_out, (torch.float32,))
+        if scales_out.shape[0] < s_shape[0] or scales_out.shape[1] < s_shape[1]:
+            raise ValueError(f"scales_out: expected at least {s_shape}, got {tuple(scales_out.shape)}")
+        scales = scales_out
+        ld_s = scales_out.stride(0)
     else:
         scales = torch.empty(s_shape, dtype=torch.float32, device=dev)
         ld_s = s_shape[1]

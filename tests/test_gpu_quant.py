@@ -211,6 +211,23 @@ def test_quant_cols_and_dual_degenerate(gpu_lib, M, C):
         assert_dual_match(gpu_lib, x, label=f"dual {M}x{C}")
 
 
+def test_quant_into_caller_buffers(gpu_lib):
+    """The binding's caller buffers (codes, and scales with a padded row
+    stride) receive exactly what the allocating call returns."""
+    x = dev(syn.activation_with_outliers(300, 640, seed=700))
+    q0, s0, _ = gpu_lib.quant_act_1x128(x, "row")
+    q = torch.full((300, 640), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((5, 320), -1.0, dtype=torch.float32, device="cuda")
+    q1, s1, _ = gpu_lib.quant_act_1x128(x, "row", out=q, scales_out=s)
+    torch.cuda.synchronize()
+    assert q1.data_ptr() == q.data_ptr() and s1.data_ptr() == s.data_ptr()
+    assert torch.equal(q, q0)
+    assert torch.equal(s[:, :300].view(torch.int32), s0[:, :300].view(torch.int32))
+    assert bool((s[:, 300:] == -1.0).all()), "scale padding columns written"
+    with pytest.raises(ValueError):
+        gpu_lib.quant_act_1x128(x, "row", out=torch.empty((300, 512), dtype=torch.uint8, device="cuda"))
+
+
 def test_quant_dual_full_size(gpu_lib):
     """dY 4096x18432: both orientations equal the separate passes everywhere
     (compared on the GPU) and the oracle on a sample of rows and columns."""
